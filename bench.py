@@ -1,0 +1,329 @@
+"""Benchmark of the block-diffusion decoding hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * block-causal attention forward and backward on the 2 x 16384-token
+    workload (16 q / 8 kv heads, head_dim 128, block 32, bf16), and
+  * one step of the batched decode loop (64 sequences with ragged prefixes
+    U[1024, 16384]): one block against the prefix cache for every sequence,
+    then the threshold commit over their [64*32 x 151936] bf16 logits and the
+    read-back of the per-block counts.
+`value` is the forward's TFLOP/s on the 16384-token workload, counted on the
+allowed (query, key) pairs only (4 * head_dim flops per pair), from HIP events
+around each forward launch.  The other rows of the metric (decode steps/s,
+commit GB/s, backward TFLOP/s) are reported beside it, together with the
+single-shot decode-step and commit kernels of the 4096-token workload, measured
+over rotating input copies so that the 256 MB Infinity Cache does not serve
+them.  The CPU oracle is timed on a bounded sample on the host.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the block-causal attention, decode and commit kernels "
+              "shard without communication (see the design notes); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_diffusion_decoding_amd as bd
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ------------------------------------------------------------------ inputs
+    wl = W.WORKLOADS["fwdbwd_L16384_bf16"]
+    B, L, Hq, Hkv, D, blk = wl.batch, wl.seqlen, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.block_size
+    inp = W.attention_inputs(B, L, Hq, Hkv, D, "bf16", wl.seed, with_grad=True)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bwd_ws = torch.empty(bd.bd_attn_bwd_workspace_size(B, L, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    pairs = blk * blk * (L // blk) * (L // blk + 1) // 2
+    fwd_flops = 4.0 * D * pairs * Hq * B
+    bwd_flops = 2.5 * fwd_flops
+
+    have_bwd = True
+    try:
+        bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
+        bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+    except bd.BdError as e:
+        if e.status != 3:
+            raise
+        have_bwd = False
+
+    # batched decode loop state (64 ragged sequences)
+    lw = W.WORKLOADS["decode_loop_bf16"]
+    rng = np.random.default_rng(lw.seed)
+    plen = W.prefix_lengths(lw.n_seq, lw.prefix_range[0], lw.prefix_range[1], rng)
+    dec = W.decode_inputs(lw.n_seq, plen, lw.block_size, Hq, Hkv, D, "bf16", lw.seed, rng=rng)
+    kc, vc = to_dev(dec["k_cache"]), to_dev(dec["v_cache"])
+    ps, pl = torch.from_numpy(dec["prefix_start"]).to(dev), torch.from_numpy(dec["prefix_len"]).to(dev)
+    qb, kb, vb = (to_dev(dec[n]) for n in ("q_blk", "k_blk", "v_blk"))
+    del dec
+    max_p = int(plen.max())
+    n_rows = lw.n_seq * lw.block_size
+    V = lw.vocab
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(lw.seed)
+    n_pool = 4
+    logit_pool = []
+    for _ in range(n_pool):   # N(0,1) + U(2,14) at one random id per row, bf16
+        x = torch.randn((n_rows, V), generator=gen, device=dev, dtype=torch.float32)
+        ids = torch.randint(0, V, (n_rows,), generator=gen, device=dev)
+        x[torch.arange(n_rows, device=dev), ids] += torch.empty(n_rows, device=dev).uniform_(
+            lw.boost[0], lw.boost[1], generator=gen)
+        logit_pool.append(x.to(torch.bfloat16))
+        del x
+    dec_o = torch.empty_like(qb)
+    dec_lse = torch.empty((lw.n_seq, Hq, lw.block_size), dtype=torch.float32, device=dev)
+    dec_ws = torch.empty(bd.bd_attn_decode_workspace_size(lw.n_seq, lw.block_size, max_p, Hq, Hkv, D),
+                         dtype=torch.uint8, device=dev)
+    com_ws = torch.empty(bd.bd_confidence_commit_workspace_size(lw.n_seq, lw.block_size, V), dtype=torch.uint8,
+                         device=dev)
+    tokens = torch.full((n_rows,), -1, dtype=torch.int32, device=dev)
+    masked = torch.ones(n_rows, dtype=torch.uint8, device=dev)
+    conf = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    pred = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    ncom = torch.empty(lw.n_seq, dtype=torch.int32, device=dev)
+    nleft = torch.empty(lw.n_seq, dtype=torch.int32, device=dev)
+    nleft_host = torch.empty(lw.n_seq, dtype=torch.int32, pin_memory=True)
+    kv_bytes_loop = float((plen.astype(np.int64) + lw.block_size).sum() * Hkv * D * 2 * 2)
+    T_step = 0.95
+    loop_state = {"step": 0}
+
+    def decode_loop_step(rec=None):
+        s = loop_state["step"]
+        if rec is not None:
+            rec[0].record()
+        bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
+        if rec is not None:
+            rec[1].record()
+        bd.bd_confidence_commit(logit_pool[s % n_pool], tokens, masked, lw.block_size, T_step, conf=conf,
+                                pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+        if rec is not None:
+            rec[2].record()
+        nleft_host.copy_(nleft, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        loop_state["step"] = s + 1
+        if int(nleft_host.sum()) == 0:          # every block committed: start the next block
+            masked.fill_(1)
+            tokens.fill_(-1)
+
+    # ------------------------------------------------------------- timed steps
+    def one_step(rec):
+        rec[0].record()
+        bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
+        rec[1].record()
+        if have_bwd:
+            bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+        rec[2].record()
+        decode_loop_step(rec[3:6])
+
+    for _ in range(args.warmup):
+        one_step([ev() for _ in range(6)])
+    torch.cuda.synchronize()
+    recs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for r in recs:
+        one_step(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [r[0].elapsed_time(r[1]) for r in recs]
+    bwd_ms = [r[1].elapsed_time(r[2]) for r in recs]
+    dec_ms = [r[3].elapsed_time(r[4]) for r in recs]
+    fwd_avg = float(np.mean(fwd_ms))
+    fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12
+
+    # ------------------------------------------- decode-loop steps/s per T
+    def full_loop(T, reps=3):
+        steps_all, t_all, commit_gbs = [], 0.0, []
+        for _ in range(reps):
+            masked.fill_(1)
+            tokens.fill_(-1)
+            torch.cuda.synchronize()
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                a, b_, c = ev(), ev(), ev()
+                a.record()
+                bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
+                b_.record()
+                m_rows = int(nleft_host.sum()) if n else n_rows
+                bd.bd_confidence_commit(logit_pool[n % n_pool], tokens, masked, lw.block_size, T, conf=conf,
+                                        pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+                c.record()
+                nleft_host.copy_(nleft, non_blocking=True)
+                torch.cuda.current_stream().synchronize()
+                commit_gbs.append(m_rows * V * 2 / (b_.elapsed_time(c) * 1e-3) / 1e9)
+                n += 1
+                if int(nleft_host.sum()) == 0 or n > 64:
+                    break
+            t_all += time.perf_counter() - t0
+            steps_all.append(n)
+        total = sum(steps_all)
+        return {"T": T, "steps_per_loop": steps_all[0], "steps_per_s": total / t_all,
+                "tokens_per_step": n_rows / steps_all[0], "commit_GBps_mean": float(np.mean(commit_gbs))}
+
+    loops = [full_loop(T) for T in lw.thresholds]
+
+    # ------------------------------- single-shot decode step / commit, 4096 prefix
+    sw = W.WORKLOADS["decode_step_bf16"]
+    n_copies_kv, n_copies_lg = 40, 64
+    srng = np.random.default_rng(sw.seed)
+    d1 = W.decode_inputs(1, [sw.prefix_len], sw.block_size, Hq, Hkv, D, "bf16", sw.seed, rng=srng)
+    c1 = W.commit_inputs(1, sw.block_size, sw.vocab, "bf16", sw.seed, boost=sw.boost, rng=srng)
+    kc1 = [to_dev(d1["k_cache"]) for _ in range(n_copies_kv)]
+    vc1 = [to_dev(d1["v_cache"]) for _ in range(n_copies_kv)]
+    qb1, kb1, vb1 = (to_dev(d1[n]) for n in ("q_blk", "k_blk", "v_blk"))
+    ps1, pl1 = torch.from_numpy(d1["prefix_start"]).to(dev), torch.from_numpy(d1["prefix_len"]).to(dev)
+    ws1 = torch.empty(bd.bd_attn_decode_workspace_size(1, sw.block_size, sw.prefix_len, Hq, Hkv, D),
+                      dtype=torch.uint8, device=dev)
+    o1 = torch.empty_like(qb1)
+    lse1 = torch.empty((1, Hq, sw.block_size), dtype=torch.float32, device=dev)
+    lg1 = [to_dev(c1["logits"]) for _ in range(n_copies_lg)]
+    tok1 = torch.from_numpy(c1["tokens"]).to(dev)
+    msk_src = torch.from_numpy(c1["masked"]).to(dev)
+    msk1 = msk_src.clone()
+    cws1 = torch.empty(bd.bd_confidence_commit_workspace_size(1, sw.block_size, sw.vocab), dtype=torch.uint8,
+                       device=dev)
+    reps = 200
+    dec_events, com_events = [], []
+    for i in range(reps + 10):
+        a, b_ = ev(), ev()
+        a.record()
+        bd.bd_attn_decode_block(qb1, kb1, vb1, kc1[i % n_copies_kv], vc1[i % n_copies_kv], ps1, pl1, sw.prefix_len,
+                                o=o1, lse=lse1, workspace=ws1)
+        b_.record()
+        if i >= 10:
+            dec_events.append((a, b_))
+    for i in range(reps + 10):
+        msk1.copy_(msk_src)
+        a, b_ = ev(), ev()
+        a.record()
+        bd.bd_confidence_commit(lg1[i % n_copies_lg], tok1, msk1, sw.block_size, sw.threshold, want_rows=False,
+                                workspace=cws1)
+        b_.record()
+        if i >= 10:
+            com_events.append((a, b_))
+    torch.cuda.synchronize()
+    dec1_us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in dec_events])
+    com1_us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in com_events])
+    dec1_bytes = (sw.prefix_len + sw.block_size) * Hkv * D * 2 * 2
+    com1_bytes = sw.block_size * sw.vocab * 2
+
+    # --------------------------------------------------------- CPU oracle sample
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    ms_per_step = wall / args.steps * 1e3
+    line = {
+        "metric": "block-causal attn TFLOP/s (%MFMA peak) at L=16384; decode steps/s; commit GB/s",
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/dO; boosted N(0,1) logits)",
+        "config": {"workload": "fwdbwd_L16384_bf16 + decode_loop_bf16 step", "batch": B, "seq_len": L,
+                   "block_size": blk, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "decode_seqs": lw.n_seq, "vocab": V},
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_d128", "flops_per_launch": fwd_flops,
+                     "avg_launch_ms": round(fwd_avg, 4)},
+        "cpu_baseline": cpu,
+        "fwd": {"TFLOPs": round(fwd_tflops, 2), "ms_mean": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4),
+                "frac_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
+        "bwd": ({"TFLOPs_2.5x": round(bwd_flops / (np.mean(bwd_ms) * 1e-3) / 1e12, 2),
+                 "ms_mean": round(float(np.mean(bwd_ms)), 4)} if have_bwd else None),
+        "decode_loop": {"kv_GB_per_step": round(kv_bytes_loop / 1e9, 3),
+                        "attn_ms_mean": round(float(np.mean(dec_ms)), 4),
+                        "attn_GBps": round(kv_bytes_loop / (np.mean(dec_ms) * 1e-3) / 1e9, 1),
+                        "by_threshold": loops},
+        "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
+                             "us_p10": round(float(np.percentile(dec1_us, 10)), 2),
+                             "us_p90": round(float(np.percentile(dec1_us, 90)), 2),
+                             "GBps": round(dec1_bytes / (np.median(dec1_us) * 1e-6) / 1e9, 1)},
+        "commit_32x151936": {"bytes": com1_bytes, "us_median": round(float(np.median(com1_us)), 2),
+                             "us_p10": round(float(np.percentile(com1_us, 10)), 2),
+                             "us_p90": round(float(np.percentile(com1_us, 90)), 2),
+                             "GBps": round(com1_bytes / (np.median(com1_us) * 1e-6) / 1e9, 1)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle forward on a bounded sample of the same workload: one (batch, head) pair,
+    query blocks taken from the end of the sequence until the time budget is spent."""
+    import workloads as W
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rng = np.random.default_rng(wl.seed)
+    L, D, blk = wl.seqlen, wl.head_dim, wl.block_size
+    q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
+    k = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
+    v = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
+    nblk = L // blk
+    done_flops, blocks = 0.0, 0
+    t0 = time.perf_counter()
+    b = nblk - 1
+    while b >= 0 and (time.perf_counter() - t0 < budget_s or blocks < 4):
+        OA.attn_fwd(q, k, v, blk, q_blocks=[b])
+        done_flops += 4.0 * D * blk * min(L, (b + 1) * blk)
+        blocks += 1
+        b -= 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 oracle forward, 1 of {wl.batch * wl.n_q_heads} (batch, head) pairs, "
+                      f"last {blocks} of {nblk} query blocks of the {L}-token workload ({done_flops / 1e9:.1f} "
+                      f"GFLOP in {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

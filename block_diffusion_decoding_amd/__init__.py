@@ -1,0 +1,170 @@
+"""Block-diffusion decoding hot path on MI355X (gfx950): Python binding of libbd.
+
+Each function has the name of the C entry point it calls (include/bd.h) and
+only marshals arguments: it reads shapes off torch tensors, allocates outputs
+and workspaces with torch when the caller passes none, and launches on the
+current HIP stream.  All computation happens in the library's HIP kernels;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (BD_BF16, BD_F32, BD_FALLBACK_NONE, BD_FALLBACK_TOP1, BdError, check, lib)
+
+__all__ = [
+    "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
+    "bd_attn_bwd_workspace_size", "bd_attn_decode_workspace_size", "bd_confidence_commit_workspace_size",
+    "BdError", "BD_F32", "BD_BF16", "BD_FALLBACK_NONE", "BD_FALLBACK_TOP1", "lib",
+]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BD_BF16
+    if t.dtype == torch.float32:
+        return BD_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if given is not None:
+        return given, given.numel() * given.element_size()
+    n = max(int(nbytes), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+# ---------------------------------------------------------------------------
+def bd_attn_fwd(q, k, v, block_size: int = 32, softmax_scale: float = 0.0, o=None, lse=None,
+                want_lse: bool = True, stream=None):
+    """Block-causal attention forward.  q [B,L,Hq,d], k/v [B,L,Hkv,d] -> (o, lse)."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q")
+    _need(k, "k", (B, L, Hkv, d), q.dtype)
+    _need(v, "v", (B, L, Hkv, d), q.dtype)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", q.shape, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", (B, Hq, L), torch.float32)
+    st = lib.bd_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, L, Hq, Hkv, d, block_size,
+                         float(softmax_scale), _dtype_code(q), _stream(stream))
+    check(st, "bd_attn_fwd")
+    return o, lse
+
+
+def bd_attn_bwd_workspace_size(batch, seqlen, n_q_heads, n_kv_heads, head_dim) -> int:
+    return int(lib.bd_attn_bwd_workspace_size(batch, seqlen, n_q_heads, n_kv_heads, head_dim))
+
+
+def bd_attn_bwd(q, k, v, o, lse, d_o, block_size: int = 32, softmax_scale: float = 0.0, dq=None, dk=None,
+                dv=None, workspace=None, stream=None):
+    """Gradients of bd_attn_fwd for the loss sum(o * d_o) -> (dq, dk, dv)."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    for t, n, shp in ((q, "q", None), (k, "k", (B, L, Hkv, d)), (v, "v", (B, L, Hkv, d)), (o, "o", q.shape),
+                      (d_o, "d_o", q.shape)):
+        _need(t, n, shp, q.dtype)
+    _need(lse, "lse", (B, Hq, L), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws, nb = _workspace(bd_attn_bwd_workspace_size(B, L, Hq, Hkv, d), q.device, workspace)
+    st = lib.bd_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                         _ptr(ws), nb, B, L, Hq, Hkv, d, block_size, float(softmax_scale), _dtype_code(q),
+                         _stream(stream))
+    check(st, "bd_attn_bwd")
+    return dq, dk, dv
+
+
+def bd_attn_decode_workspace_size(n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim) -> int:
+    return int(lib.bd_attn_decode_workspace_size(n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim))
+
+
+def bd_attn_decode_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_start, prefix_len, max_prefix_len: int,
+                         softmax_scale: float = 0.0, o=None, lse=None, want_lse: bool = True, workspace=None,
+                         stream=None):
+    """One block per sequence against its prefix cache -> (o, lse)."""
+    n, T, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    _need(q_blk, "q_blk")
+    _need(k_blk, "k_blk", (n, T, Hkv, d), q_blk.dtype)
+    _need(v_blk, "v_blk", (n, T, Hkv, d), q_blk.dtype)
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t is not None:
+            _need(t, name, None, q_blk.dtype)
+    _need(prefix_start, "prefix_start", (n,), torch.int64)
+    _need(prefix_len, "prefix_len", (n,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q_blk)
+    if lse is None and want_lse:
+        lse = torch.empty((n, Hq, T), dtype=torch.float32, device=q_blk.device)
+    ws, nb = _workspace(bd_attn_decode_workspace_size(n, T, max_prefix_len, Hq, Hkv, d), q_blk.device, workspace)
+    st = lib.bd_attn_decode_block(_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(prefix_start), _ptr(prefix_len), int(max_prefix_len), _ptr(o), _ptr(lse),
+                                  n, T, Hq, Hkv, d, float(softmax_scale), _dtype_code(q_blk), _ptr(ws), nb,
+                                  _stream(stream))
+    check(st, "bd_attn_decode_block")
+    return o, lse
+
+
+def bd_confidence_commit_workspace_size(n_seq, blk_len, vocab) -> int:
+    return int(lib.bd_confidence_commit_workspace_size(n_seq, blk_len, vocab))
+
+
+def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold: float, fallback: int = BD_FALLBACK_TOP1,
+                         vocab: Optional[int] = None, conf=None, pred=None, n_committed=None, n_masked_left=None,
+                         want_rows: bool = True, workspace=None, stream=None):
+    """Threshold commit; updates ``tokens``/``masked`` in place.
+
+    logits [rows, >= vocab] (row stride = logits.stride(0)); tokens int32 [rows];
+    masked uint8 [rows].  Returns dict(conf, pred, n_committed, n_masked_left).
+    """
+    rows = logits.shape[0]
+    if rows % blk_len:
+        raise ValueError("logits rows must be a multiple of blk_len")
+    n_seq = rows // blk_len
+    V = logits.shape[1] if vocab is None else int(vocab)
+    if not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
+    _need(tokens, "tokens", (rows,), torch.int32)
+    _need(masked, "masked", (rows,), torch.uint8)
+    dev = logits.device
+    if want_rows:
+        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
+        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
+    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
+    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    ws, nb = _workspace(bd_confidence_commit_workspace_size(n_seq, blk_len, V), dev, workspace)
+    st = lib.bd_confidence_commit(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
+                                  float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred),
+                                  _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
+    check(st, "bd_confidence_commit")
+    return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}

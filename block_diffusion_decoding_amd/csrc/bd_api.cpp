@@ -1,0 +1,174 @@
+// C ABI of libbd: argument validation and dispatch to the HIP launchers.
+// Every check here runs on the host before anything is enqueued, so the error
+// paths need no GPU.  The entry points are declared, with their contracts, in
+// include/bd.h.
+#include "bd.h"
+#include "bd_kernels.hpp"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+bd_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return BD_OK;
+  g_last_hip_error = (int)e;
+  return BD_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
+
+bd_status check_attn_shape(int batch, int seqlen, int hq, int hkv, int d, int blk, bd_dtype dtype, float scale) {
+  if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || blk <= 0) return BD_ERR_SHAPE;
+  if (hq % hkv != 0) return BD_ERR_SHAPE;
+  if (std::isnan(scale) || std::isinf(scale)) return BD_ERR_VALUE;
+  if (dtype == BD_BF16) {
+    if (d != 128) return BD_ERR_UNSUPPORTED;
+  } else if (dtype == BD_F32) {
+    if (d > 128) return BD_ERR_UNSUPPORTED;
+  } else {
+    return BD_ERR_UNSUPPORTED;
+  }
+  if ((long long)batch * hq * seqlen > kMaxGrid) return BD_ERR_SHAPE;
+  return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bd_status_string(bd_status s) {
+  switch (s) {
+    case BD_OK: return "ok";
+    case BD_ERR_NULL: return "required pointer is NULL";
+    case BD_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case BD_ERR_UNSUPPORTED: return "dtype / head_dim combination not supported";
+    case BD_ERR_WORKSPACE: return "workspace missing or too small";
+    case BD_ERR_VALUE: return "scalar argument out of its domain";
+    case BD_ERR_HIP: return "HIP runtime error";
+    case BD_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+int bd_last_hip_error(void) { return g_last_hip_error; }
+
+int bd_version(void) { return 100; }
+
+bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int seqlen,
+                      int n_q_heads, int n_kv_heads, int head_dim, int block_size, float softmax_scale,
+                      bd_dtype dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o) return BD_ERR_NULL;
+  bd_status st = check_attn_shape(batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size, dtype, softmax_scale);
+  if (st != BD_OK) return st;
+  bd::AttnShape s{batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size,
+                  resolve_scale(softmax_scale, head_dim)};
+  if (dtype == BD_BF16) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BD_ERR_ALIGNMENT;
+    return hip_status(bd::launch_attn_fwd_bf16(q, k, v, o, lse, s, stream));
+  }
+  return hip_status(bd::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                            static_cast<const float*>(v), static_cast<float*>(o), lse, s,
+                                            stream));
+}
+
+size_t bd_attn_bwd_workspace_size(int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim) {
+  (void)n_kv_heads;
+  (void)head_dim;
+  if (batch <= 0 || seqlen <= 0 || n_q_heads <= 0) return 0;
+  return bd::attn_bwd_workspace_bytes(batch, seqlen, n_q_heads);
+}
+
+bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* d_o, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int batch,
+                      int seqlen, int n_q_heads, int n_kv_heads, int head_dim, int block_size,
+                      float softmax_scale, bd_dtype dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return BD_ERR_NULL;
+  bd_status st = check_attn_shape(batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size, dtype, softmax_scale);
+  if (st != BD_OK) return st;
+  const size_t need = bd::attn_bwd_workspace_bytes(batch, seqlen, n_q_heads);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  bd::AttnShape s{batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size,
+                  resolve_scale(softmax_scale, head_dim)};
+  if (dtype == BD_BF16) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+      return BD_ERR_ALIGNMENT;
+    const hipError_t e = bd::launch_attn_bwd_bf16(q, k, v, o, lse, d_o, dq, dk, dv, workspace, s, stream);
+    if (e == hipErrorNotSupported) return BD_ERR_UNSUPPORTED;
+    return hip_status(e);
+  }
+  return hip_status(bd::launch_attn_bwd_f32(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(o), lse, static_cast<const float*>(d_o), static_cast<float*>(dq),
+      static_cast<float*>(dk), static_cast<float*>(dv), workspace, s, stream));
+}
+
+size_t bd_attn_decode_workspace_size(int n_seq, int blk_len, int max_prefix_len, int n_q_heads, int n_kv_heads,
+                                     int head_dim) {
+  if (n_seq <= 0 || blk_len <= 0 || max_prefix_len < 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+      n_q_heads % n_kv_heads != 0 || head_dim <= 0)
+    return 0;
+  bd::DecodeShape s{n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim, 1.f};
+  return bd::decode_workspace_bytes(s, 1);
+}
+
+bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
+                               const void* v_cache, const int64_t* prefix_start, const int32_t* prefix_len,
+                               int max_prefix_len, void* o, float* lse, int n_seq, int blk_len, int n_q_heads,
+                               int n_kv_heads, int head_dim, float softmax_scale, bd_dtype dtype, void* workspace,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (!q_blk || !k_blk || !v_blk || !o || !prefix_start || !prefix_len) return BD_ERR_NULL;
+  if (max_prefix_len > 0 && (!k_cache || !v_cache)) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || max_prefix_len < 0) return BD_ERR_SHAPE;
+  bd_status st = check_attn_shape(n_seq, blk_len, n_q_heads, n_kv_heads, head_dim, 1, dtype, softmax_scale);
+  if (st != BD_OK) return st;
+  if ((long long)max_prefix_len + blk_len > kMaxGrid / 2) return BD_ERR_SHAPE;
+  bd::DecodeShape s{n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim,
+                    resolve_scale(softmax_scale, head_dim)};
+  if (dtype == BD_BF16) {
+    if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+        (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)))
+      return BD_ERR_ALIGNMENT;
+    const size_t need = bd::decode_workspace_bytes(s, 1);
+    if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+    return hip_status(bd::launch_decode_bf16(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_start, prefix_len, o,
+                                             lse, workspace, s, stream));
+  }
+  return hip_status(bd::launch_decode_f32(
+      static_cast<const float*>(q_blk), static_cast<const float*>(k_blk), static_cast<const float*>(v_blk),
+      static_cast<const float*>(k_cache), static_cast<const float*>(v_cache), prefix_start, prefix_len,
+      static_cast<float*>(o), lse, s, stream));
+}
+
+size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab) {
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  return bd::commit_workspace_bytes(n_seq, blk_len, vocab, 1);
+}
+
+bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                               bd_dtype dtype, float threshold, bd_fallback fallback, int32_t* tokens,
+                               uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
+                               int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !tokens || !masked) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || row_stride < vocab) return BD_ERR_SHAPE;
+  if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
+  if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
+  if (std::isnan(threshold)) return BD_ERR_VALUE;
+  if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
+  const long long rows = (long long)n_seq * blk_len;
+  if (rows * bd::commit_chunks_per_row(vocab, dtype == BD_BF16) > kMaxGrid) return BD_ERR_SHAPE;
+  const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab, dtype == BD_BF16);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold,
+                   fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
+  return hip_status(bd::launch_commit(a, stream));
+}
+
+}  // extern "C"

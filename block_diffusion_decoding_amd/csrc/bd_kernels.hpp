@@ -1,0 +1,67 @@
+// Host-side launchers of the libbd kernels.  Arguments have been validated by
+// the C-ABI layer (bd_api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+struct AttnShape {
+  int batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size;
+  float scale;  // resolved softmax scale (> 0)
+};
+
+// ---- full-sequence block-causal attention ---------------------------------
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const AttnShape& s, hipStream_t st);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               const AttnShape& s, hipStream_t st);
+
+size_t attn_bwd_workspace_bytes(int batch, int seqlen, int n_q_heads);
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                                void* ws, const AttnShape& s, hipStream_t st);
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                               const float* lse, const float* d_o, float* dq, float* dk, float* dv,
+                               void* ws, const AttnShape& s, hipStream_t st);
+
+// ---- one block against a prefix KV cache -----------------------------------
+struct DecodeShape {
+  int n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim;
+  float scale;
+};
+size_t decode_workspace_bytes(const DecodeShape& s, int is_bf16);
+hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* v_blk,
+                              const void* k_cache, const void* v_cache, const int64_t* prefix_start,
+                              const int32_t* prefix_len, void* o, float* lse, void* ws,
+                              const DecodeShape& s, hipStream_t st);
+hipError_t launch_decode_f32(const float* q_blk, const float* k_blk, const float* v_blk,
+                             const float* k_cache, const float* v_cache, const int64_t* prefix_start,
+                             const int32_t* prefix_len, float* o, float* lse, const DecodeShape& s,
+                             hipStream_t st);
+
+// ---- confidence-threshold commit -------------------------------------------
+struct CommitArgs {
+  const void* logits;
+  int64_t row_stride;
+  int n_seq, blk_len, vocab;
+  int is_bf16;
+  float threshold;
+  int fallback_top1;
+  int32_t* tokens;
+  uint8_t* masked;
+  float* conf;
+  int32_t* pred;
+  int32_t* n_committed;
+  int32_t* n_masked_left;
+  void* ws;
+};
+int commit_chunks_per_row(int vocab, int is_bf16);
+size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab, int is_bf16);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+
+constexpr int kCommitMaxBlock = 1024;  // largest blk_len the commit kernel takes
+
+}  // namespace bd

@@ -1,0 +1,188 @@
+/*
+ * bd.h -- C ABI of the block-diffusion decoding hot path on MI355X (gfx950).
+ *
+ * The method (MinerU-Diffusion) decodes the output token sequence block by
+ * block.  Inside a block of L' tokens every token attends to every other token
+ * of the block; across blocks attention is causal: a token attends to all
+ * earlier blocks and to no later block (paper.rainbus.top digest, method step
+ * 3; hysenlabs.com editorial "The idea: OCR as inverse rendering"; OpenDataLab
+ * blog, Fig. 2).  The earlier blocks are held as a KV cache (digest, novelty
+ * paragraph).  After each denoising step every still-masked position whose
+ * prediction confidence exceeds a threshold T is confirmed (digest, method
+ * steps 4 and 6: T = 0.95, temperature 1, no top-k / top-p).
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer argument is DEVICE memory owned by the caller.  The library
+ *     never allocates or frees memory; scratch space is the caller's
+ *     `workspace`, sized by the matching *_workspace_size() query.
+ *   - Tensors are dense and row-major with the innermost dimension last:
+ *     q/o [batch, seqlen, n_q_heads, head_dim], k/v [batch, seqlen, n_kv_heads,
+ *     head_dim] ("BSHD"); lse [batch, n_q_heads, seqlen] float32, natural log.
+ *   - `dtype` selects the element type of q/k/v/o/dO/dq/dk/dv and logits:
+ *     BD_F32 (float32) or BD_BF16 (bfloat16).  Accumulation is float32.
+ *   - Grouped-query attention: query head h reads KV head h / (n_q_heads /
+ *     n_kv_heads); n_q_heads must be a multiple of n_kv_heads.
+ *   - softmax_scale <= 0 selects 1/sqrt(head_dim); a NaN scale is BD_ERR_VALUE.
+ *   - bf16 tensors (and float32 logits) are read with 16-byte vector loads: their
+ *     base pointers must be 16-byte aligned (BD_ERR_ALIGNMENT otherwise;
+ *     logits fall back to scalar loads instead).
+ *   - Calls are asynchronous: they validate the arguments, enqueue kernels on
+ *     `stream` and return.  A non-BD_OK status means nothing was enqueued,
+ *     except BD_ERR_HIP, which reports a failed launch (bd_last_hip_error()
+ *     gives the hipError_t).  Faults inside a kernel surface at the caller's
+ *     next synchronisation.
+ *   - The library keeps no mutable global state except a thread-local last HIP
+ *     error; calls on different streams may run concurrently as long as their
+ *     output and workspace buffers do not overlap.
+ */
+#ifndef BD_H_
+#define BD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BD_OK = 0,
+  BD_ERR_NULL = 1,         /* a required pointer is NULL */
+  BD_ERR_SHAPE = 2,        /* a size is non-positive or inconsistent */
+  BD_ERR_UNSUPPORTED = 3,  /* dtype / head_dim combination not compiled in */
+  BD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query returns */
+  BD_ERR_VALUE = 5,        /* a scalar argument is out of its domain (e.g. NaN threshold) */
+  BD_ERR_HIP = 6,          /* a HIP runtime call failed */
+  BD_ERR_ALIGNMENT = 7     /* a bf16 tensor pointer is not 16-byte aligned */
+} bd_status;
+
+typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+
+/* What a block does when none of its masked tokens clears the threshold. */
+typedef enum {
+  BD_FALLBACK_NONE = 0,  /* commit nothing; the block stays as it is */
+  BD_FALLBACK_TOP1 = 1   /* commit the single most confident masked token (lowest row on ties) */
+} bd_fallback;
+
+/* ------------------------------------------------------------------------
+ * Block-causal attention over whole sequences (training / prefill).
+ *
+ * Query i may attend key j exactly when floor(j / block_size) <=
+ * floor(i / block_size) (digest, method step 3).  seqlen need not be a
+ * multiple of block_size: the last block is then short.
+ *
+ *   q  [batch, seqlen, n_q_heads, head_dim]   in
+ *   k  [batch, seqlen, n_kv_heads, head_dim]  in
+ *   v  [batch, seqlen, n_kv_heads, head_dim]  in
+ *   o  [batch, seqlen, n_q_heads, head_dim]   out
+ *   lse [batch, n_q_heads, seqlen] float32    out, may be NULL (natural-log
+ *        log-sum-exp of the scaled scores of each row; bd_attn_bwd needs it)
+ *
+ * Supported: BD_BF16 with head_dim 128 (matrix-core path); BD_F32 with
+ * head_dim <= 128 (vector path).
+ * ---------------------------------------------------------------------- */
+bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim,
+                      int block_size, float softmax_scale, bd_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Gradients of bd_attn_fwd for the loss sum(o * d_o) (the masked-token
+ * training objective of the blog's Fig. 2 back-propagates through this).
+ *
+ *   q, k, v, o, lse   as produced / consumed by bd_attn_fwd (lse required)
+ *   d_o [batch, seqlen, n_q_heads, head_dim]       in
+ *   dq  [batch, seqlen, n_q_heads, head_dim]       out
+ *   dk, dv [batch, seqlen, n_kv_heads, head_dim]   out (summed over the query
+ *        heads of each group)
+ *   workspace of bd_attn_bwd_workspace_size() bytes (holds the per-row
+ *        D = rowsum(d_o * o) in float32); contents on entry are ignored.
+ *
+ * Supported: as bd_attn_fwd.  Deterministic: no atomics.
+ * ---------------------------------------------------------------------- */
+size_t bd_attn_bwd_workspace_size(int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim);
+bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* d_o, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                      int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim,
+                      int block_size, float softmax_scale, bd_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One block per sequence against that sequence's KV-cache prefix (one
+ * denoising step of decoding; digest, novelty paragraph on KV-cache reuse).
+ *
+ * The block is the newest block of its sequence, so each of its tokens sees
+ * every prefix token and every token of the block: keys are
+ * cache[prefix_start[s] .. prefix_start[s] + prefix_len[s]) followed by the
+ * block's own k_blk/v_blk rows, all unmasked.
+ *
+ *   q_blk [n_seq, blk_len, n_q_heads, head_dim]     in
+ *   k_blk, v_blk [n_seq, blk_len, n_kv_heads, head_dim]  in (the block's own
+ *        keys and values, recomputed by the model at every step)
+ *   k_cache, v_cache [total_rows, n_kv_heads, head_dim]  in (packed, ragged;
+ *        may be NULL only if every prefix_len is 0)
+ *   prefix_start int64[n_seq], prefix_len int32[n_seq]  in, DEVICE memory;
+ *        prefix_len[s] must lie in [0, max_prefix_len]
+ *   max_prefix_len  host value, an upper bound of prefix_len (sizes the grid)
+ *   o [n_seq, blk_len, n_q_heads, head_dim]        out
+ *   lse [n_seq, n_q_heads, blk_len] float32        out, may be NULL
+ *   workspace of bd_attn_decode_workspace_size() bytes (split-KV partial
+ *        softmax states); contents on entry are ignored.
+ *
+ * Supported: as bd_attn_fwd.
+ * ---------------------------------------------------------------------- */
+size_t bd_attn_decode_workspace_size(int n_seq, int blk_len, int max_prefix_len,
+                                     int n_q_heads, int n_kv_heads, int head_dim);
+bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void* v_blk,
+                               const void* k_cache, const void* v_cache,
+                               const int64_t* prefix_start, const int32_t* prefix_len, int max_prefix_len,
+                               void* o, float* lse, int n_seq, int blk_len,
+                               int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
+                               bd_dtype dtype, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Confidence-threshold commit (digest, method steps 4 and 6).
+ *
+ * logits [n_seq * blk_len rows, vocab], row r at logits + r * row_stride
+ * elements (row_stride >= vocab).  Rows r = s * blk_len .. s * blk_len +
+ * blk_len - 1 form the current block of sequence s.
+ *
+ * For each row with masked[r] != 0 on entry:
+ *   pred[r] = lowest id v with logits[r][v] = max_v logits[r][v]
+ *   conf[r] = 1 / sum_v exp(logits[r][v] - max)   (largest softmax probability
+ *             at temperature 1 over the full vocabulary)
+ *   A row holding NaN or +Inf, or only -Inf, gets conf = NaN and pred = -1.
+ * Then per block s: the rows with conf > threshold (strict) are committed; if
+ * there are none and fallback == BD_FALLBACK_TOP1, the masked row with the
+ * largest non-NaN conf is committed (lowest row on ties).  Committing row r
+ * sets tokens[r] = pred[r] and masked[r] = 0.
+ *
+ *   tokens int32[n_seq*blk_len], masked uint8[n_seq*blk_len]   in/out
+ *   conf float32[n_seq*blk_len], pred int32[n_seq*blk_len]     out, may be
+ *        NULL; written only for rows masked on entry
+ *   n_committed, n_masked_left int32[n_seq]                    out, may be NULL
+ *   workspace of bd_confidence_commit_workspace_size() bytes; contents on
+ *        entry are ignored.
+ * Rows with masked[r] == 0 on entry are neither read nor written.  A
+ * threshold outside (0, 1) is legal (>= 1: fallback only; < 1/vocab: every
+ * masked row commits); a NaN threshold is BD_ERR_VALUE.
+ * ---------------------------------------------------------------------- */
+size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab);
+bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                               bd_dtype dtype, float threshold, bd_fallback fallback,
+                               int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred,
+                               int32_t* n_committed, int32_t* n_masked_left,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* bd_status_string(bd_status s);
+
+/* hipError_t of the most recent BD_ERR_HIP returned on the calling thread. */
+int bd_last_hip_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int bd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BD_H_ */

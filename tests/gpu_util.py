@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU parity tests: host <-> device moves and the commit grader."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    """bf16 bit array (uint16) -> device bfloat16 tensor with the same values."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    return dev_bf16(x) if dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host_vals(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact values an input array stands for, in float64 (what the oracle reads)."""
+    return W.bf16_bits_to_f32(x).astype(np.float64) if dtype == "bf16" else x.astype(np.float64)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def banner(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+
+
+def grade_commit(ref: dict, gpu: dict, masked_in: np.ndarray, tokens_in: np.ndarray, blk_len: int, T: float,
+                 fallback_top1: bool = True, band: float = 1e-4, conf_rtol: float = 1e-5):
+    """Compare one GPU commit step with the oracle's.
+
+    Ids and masks must match bit for bit, except in groups where the oracle's confidence
+    of some row lies within ``band`` of T (near-T rows), or where the fallback choice is
+    decided by confidences within ``band`` of each other; such groups are counted and
+    only their validity is checked.  Returns (n_near_rows, n_ambiguous_groups).
+    """
+    m_in = masked_in.astype(bool)
+    assert np.array_equal(gpu["pred"][m_in], ref["pred"][m_in]), "argmax ids differ"
+    cr, cg = ref["conf"][m_in], gpu["conf"][m_in]
+    assert np.array_equal(np.isnan(cr), np.isnan(cg)), "invalid-row flags differ"
+    ok = ~np.isnan(cr)
+    if ok.any():
+        err = np.abs(cg[ok] - cr[ok])
+        assert np.all(err <= conf_rtol * cr[ok] + 1e-7), f"conf max rel err {np.max(err / cr[ok])}"
+    assert np.array_equal(gpu["tokens"][~m_in], tokens_in[~m_in]), "unmasked rows touched"
+    assert np.array_equal(gpu["masked"][~m_in], masked_in[~m_in]), "unmasked rows touched"
+    committed = m_in & (gpu["masked"] == 0)
+    assert np.array_equal(gpu["tokens"][committed], gpu["pred"][committed])
+    assert np.array_equal(gpu["tokens"][m_in & ~committed], tokens_in[m_in & ~committed])
+    near_rows, ambiguous = 0, 0
+    for g in range(len(masked_in) // blk_len):
+        sl = slice(g * blk_len, (g + 1) * blk_len)
+        mg, c, com_g, com_r = m_in[sl], ref["conf"][sl], committed[sl], ref["committed"][sl]
+        valid = mg & ~np.isnan(c)
+        near = valid & (np.abs(c - T) <= band)
+        near_rows += int(near.sum())
+        assert gpu["n_committed"][g] == com_g.sum()
+        assert gpu["n_masked_left"][g] == mg.sum() - com_g.sum()
+        if near.any():
+            ambiguous += 1
+            assert np.all(com_g[valid & (c > T + band)]), f"group {g}: a row far above T was not committed"
+            if com_g.sum() > 1:
+                assert not np.any(com_g & valid & (c < T - band)), f"group {g}: a row far below T was committed"
+            continue
+        if (valid & (c > T)).any() or not fallback_top1 or not valid.any():
+            assert np.array_equal(com_g, com_r), f"group {g}: committed set differs"
+            continue
+        cv = np.where(valid, c, -np.inf)
+        top = np.sort(cv)[::-1]
+        if len(top) > 1 and top[0] - top[1] <= band:
+            ambiguous += 1
+            assert com_g.sum() == 1 and cv[np.flatnonzero(com_g)[0]] >= top[0] - band
+        else:
+            assert np.array_equal(com_g, com_r), f"group {g}: fallback row differs"
+    return near_rows, ambiguous

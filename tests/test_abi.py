@@ -1,0 +1,127 @@
+"""The C-ABI library: it loads, exports every entry point include/bd.h declares, and rejects
+bad arguments on the host before anything is enqueued (no GPU needed: every call below
+fails validation, so no kernel is launched)."""
+import math
+import os
+import re
+
+import pytest
+
+from block_diffusion_decoding_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a 16-byte aligned, never dereferenced stand-in address
+MIS = FAKE + 8          # misaligned stand-in
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "bd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L.lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        assert L.lib.bd_status_string(s)
+    assert L.lib.bd_status_string(99) == b"unknown status"
+    assert L.lib.bd_version() >= 100
+
+
+def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, S=64, Hq=2, Hkv=1, d=128, blk=32, sc=0.0, dt=L.BD_BF16):
+    return L.lib.bd_attn_fwd(q, k, v, o, lse, B, S, Hq, Hkv, d, blk, sc, dt, None)
+
+
+def test_fwd_validation():
+    assert fwd(q=None) == L.BD_ERR_NULL
+    assert fwd(o=None) == L.BD_ERR_NULL
+    assert fwd(B=0) == L.BD_ERR_SHAPE
+    assert fwd(S=-1) == L.BD_ERR_SHAPE
+    assert fwd(blk=0) == L.BD_ERR_SHAPE
+    assert fwd(Hq=3, Hkv=2) == L.BD_ERR_SHAPE
+    assert fwd(d=64) == L.BD_ERR_UNSUPPORTED
+    assert fwd(d=256, dt=L.BD_F32) == L.BD_ERR_UNSUPPORTED
+    assert fwd(dt=7) == L.BD_ERR_UNSUPPORTED
+    assert fwd(sc=math.nan) == L.BD_ERR_VALUE
+    assert fwd(sc=math.inf) == L.BD_ERR_VALUE
+    assert fwd(k=MIS) == L.BD_ERR_ALIGNMENT
+    assert fwd(o=MIS) == L.BD_ERR_ALIGNMENT
+
+
+def test_bwd_validation():
+    ws = L.lib.bd_attn_bwd_workspace_size(1, 64, 2, 1, 128)
+    assert ws == 1 * 2 * 64 * 4
+    args = [FAKE] * 9 + [FAKE, ws, 1, 64, 2, 1, 128, 32, 0.0, L.BD_BF16, None]
+    bad = list(args); bad[4] = None
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_NULL          # lse is required
+    bad = list(args); bad[9] = None
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_WORKSPACE
+    bad = list(args); bad[10] = ws - 4
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_WORKSPACE
+    bad = list(args); bad[14] = 3
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_SHAPE
+    bad = list(args); bad[5] = MIS
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_ALIGNMENT
+
+
+def test_decode_validation():
+    ws = L.lib.bd_attn_decode_workspace_size(1, 32, 4096, 16, 8, 128)
+    assert ws > 0
+    assert L.lib.bd_attn_decode_workspace_size(1, 32, 4096, 16, 6, 128) == 0
+
+    def call(**kw):
+        a = dict(qb=FAKE, kb=FAKE, vb=FAKE, kc=FAKE, vc=FAKE, ps=FAKE, pl=FAKE, maxp=4096, o=FAKE, lse=None,
+                 n=1, T=32, Hq=16, Hkv=8, d=128, sc=0.0, dt=L.BD_BF16, ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_attn_decode_block(a["qb"], a["kb"], a["vb"], a["kc"], a["vc"], a["ps"], a["pl"], a["maxp"],
+                                          a["o"], a["lse"], a["n"], a["T"], a["Hq"], a["Hkv"], a["d"], a["sc"],
+                                          a["dt"], a["ws"], a["nb"], None)
+    assert call(qb=None) == L.BD_ERR_NULL
+    assert call(ps=None) == L.BD_ERR_NULL
+    assert call(kc=None) == L.BD_ERR_NULL
+    assert call(maxp=-1) == L.BD_ERR_SHAPE
+    assert call(n=0) == L.BD_ERR_SHAPE
+    assert call(Hkv=6) == L.BD_ERR_SHAPE
+    assert call(d=96) == L.BD_ERR_UNSUPPORTED
+    assert call(ws=None) == L.BD_ERR_WORKSPACE
+    assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+    assert call(kc=MIS) == L.BD_ERR_ALIGNMENT
+    assert call(sc=math.nan) == L.BD_ERR_VALUE
+
+
+def test_commit_validation():
+    ws = L.lib.bd_confidence_commit_workspace_size(2, 32, 151936)
+    assert ws == 2 * 32 * 19 * 16
+
+    def call(**kw):
+        a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, thr=0.95, fb=1, tok=FAKE, msk=FAKE,
+                 ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_confidence_commit(a["lg"], a["stride"], a["n"], a["T"], a["V"], a["dt"], a["thr"], a["fb"],
+                                          a["tok"], a["msk"], None, None, None, None, a["ws"], a["nb"], None)
+    assert call(lg=None) == L.BD_ERR_NULL
+    assert call(tok=None) == L.BD_ERR_NULL
+    assert call(msk=None) == L.BD_ERR_NULL
+    assert call(stride=100) == L.BD_ERR_SHAPE
+    assert call(V=0) == L.BD_ERR_SHAPE
+    assert call(T=2048) == L.BD_ERR_UNSUPPORTED
+    assert call(dt=5) == L.BD_ERR_UNSUPPORTED
+    assert call(thr=math.nan) == L.BD_ERR_VALUE
+    assert call(fb=7) == L.BD_ERR_VALUE
+    assert call(ws=None) == L.BD_ERR_WORKSPACE
+    assert call(nb=ws - 16) == L.BD_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    import block_diffusion_decoding_amd as bd
+    x = torch.zeros(1, 32, 1, 64)
+    with pytest.raises(ValueError):
+        bd.bd_attn_fwd(x, x, x)
