@@ -127,52 +127,87 @@ def main():
     T_step = 0.95
     loop_state = {"step": 0}
 
-    def decode_loop_step(rec=None):
+    def one_step(rec):
+        """decode + commit for every sequence, then forward + backward; one sync at the end."""
         s = loop_state["step"]
-        if rec is not None:
-            rec[0].record()
+        rec[0].record()
         bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
-        if rec is not None:
-            rec[1].record()
+        rec[1].record()
         bd.bd_confidence_commit(logit_pool[s % n_pool], tokens, masked, lw.block_size, T_step, conf=conf,
                                 pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
-        if rec is not None:
-            rec[2].record()
+        rec[2].record()
+        bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
+        rec[3].record()
+        if have_bwd:
+            bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+        rec[4].record()
         nleft_host.copy_(nleft, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         loop_state["step"] = s + 1
-        if int(nleft_host.sum()) == 0:          # every block committed: start the next block
+        if int(nleft_host.sum()) == 0:          # every block committed: the next block starts masked
             masked.fill_(1)
             tokens.fill_(-1)
 
-    # ------------------------------------------------------------- timed steps
-    def one_step(rec):
-        rec[0].record()
-        bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
-        rec[1].record()
-        if have_bwd:
-            bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
-        rec[2].record()
-        decode_loop_step(rec[3:6])
-
     for _ in range(args.warmup):
-        one_step([ev() for _ in range(6)])
+        one_step([ev() for _ in range(5)])
     torch.cuda.synchronize()
-    recs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    recs = [[ev() for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for r in recs:
         one_step(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [r[0].elapsed_time(r[1]) for r in recs]
-    bwd_ms = [r[1].elapsed_time(r[2]) for r in recs]
-    dec_ms = [r[3].elapsed_time(r[4]) for r in recs]
+    fwd_ms = [r[2].elapsed_time(r[3]) for r in recs]
+    bwd_ms = [r[3].elapsed_time(r[4]) for r in recs]
     fwd_avg = float(np.mean(fwd_ms))
     fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12
 
+    def primed(launches, n_launch_us=60.0):
+        """Per-launch GPU time of short kernels: a spin kernel holds the queue while the host
+        enqueues every launch with its events, so no launch waits on the host."""
+        evs = [(ev(), ev()) for _ in launches]
+        spin_ms = len(launches) * n_launch_us * 1e-3
+        torch.cuda._sleep(int(spin_ms * 1e-3 * sleep_hz))
+        for (a, b_), fn in zip(evs, launches):
+            a.record()
+            fn()
+            b_.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b_) * 1e3 for a, b_ in evs])
+
+    # calibrate the spin kernel
+    a0, b0 = ev(), ev()
+    a0.record()
+    torch.cuda._sleep(1_000_000)
+    b0.record()
+    torch.cuda.synchronize()
+    sleep_hz = 1_000_000 / (a0.elapsed_time(b0) * 1e-3)
+
+    # decode-loop kernels, primed: one full loop at T = 0.95 with per-launch GPU times
+    masked.fill_(1)
+    tokens.fill_(-1)
+    dec_us, com_us, com_rows = [], [], []
+    for step in range(64):
+        m_rows = int(masked.sum())
+        if m_rows == 0:
+            break
+        t_us = primed([lambda: bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse,
+                                                       workspace=dec_ws),
+                       lambda st=step: bd.bd_confidence_commit(logit_pool[st % n_pool], tokens, masked,
+                                                               lw.block_size, T_step, conf=conf, pred=pred,
+                                                               n_committed=ncom, n_masked_left=nleft,
+                                                               workspace=com_ws)])
+        dec_us.append(t_us[0])
+        com_us.append(t_us[1])
+        com_rows.append(m_rows)
+    dec_ms = np.array(dec_us) * 1e-3
+    com_gbs_loop = [r * V * 2 / (u * 1e-6) / 1e9 for r, u in zip(com_rows, com_us)]
+
     # ------------------------------------------- decode-loop steps/s per T
     def full_loop(T, reps=3):
-        steps_all, t_all, commit_gbs = [], 0.0, []
+        """Whole loops from an all-masked block until every sequence's block is committed;
+        wall-clock steps/s including the per-step read-back of the block counts."""
+        steps_all, t_all = [], 0.0
         for _ in range(reps):
             masked.fill_(1)
             tokens.fill_(-1)
@@ -180,25 +215,18 @@ def main():
             n = 0
             t0 = time.perf_counter()
             while True:
-                a, b_, c = ev(), ev(), ev()
-                a.record()
                 bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
-                b_.record()
-                m_rows = int(nleft_host.sum()) if n else n_rows
                 bd.bd_confidence_commit(logit_pool[n % n_pool], tokens, masked, lw.block_size, T, conf=conf,
                                         pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
-                c.record()
                 nleft_host.copy_(nleft, non_blocking=True)
                 torch.cuda.current_stream().synchronize()
-                commit_gbs.append(m_rows * V * 2 / (b_.elapsed_time(c) * 1e-3) / 1e9)
                 n += 1
-                if int(nleft_host.sum()) == 0 or n > 64:
+                if int(nleft_host.sum()) == 0 or n >= 4 * lw.block_size:
                     break
             t_all += time.perf_counter() - t0
             steps_all.append(n)
-        total = sum(steps_all)
-        return {"T": T, "steps_per_loop": steps_all[0], "steps_per_s": total / t_all,
-                "tokens_per_step": n_rows / steps_all[0], "commit_GBps_mean": float(np.mean(commit_gbs))}
+        return {"T": T, "steps_per_block": steps_all[0], "steps_per_s": round(sum(steps_all) / t_all, 1),
+                "tokens_per_s": round(n_rows * reps / t_all, 1)}
 
     loops = [full_loop(T) for T in lw.thresholds]
 
@@ -219,31 +247,24 @@ def main():
     lg1 = [to_dev(c1["logits"]) for _ in range(n_copies_lg)]
     tok1 = torch.from_numpy(c1["tokens"]).to(dev)
     msk_src = torch.from_numpy(c1["masked"]).to(dev)
-    msk1 = msk_src.clone()
+    msk1 = [msk_src.clone() for _ in range(n_copies_lg)]
     cws1 = torch.empty(bd.bd_confidence_commit_workspace_size(1, sw.block_size, sw.vocab), dtype=torch.uint8,
                        device=dev)
-    reps = 200
-    dec_events, com_events = [], []
-    for i in range(reps + 10):
-        a, b_ = ev(), ev()
-        a.record()
-        bd.bd_attn_decode_block(qb1, kb1, vb1, kc1[i % n_copies_kv], vc1[i % n_copies_kv], ps1, pl1, sw.prefix_len,
-                                o=o1, lse=lse1, workspace=ws1)
-        b_.record()
-        if i >= 10:
-            dec_events.append((a, b_))
-    for i in range(reps + 10):
-        msk1.copy_(msk_src)
-        a, b_ = ev(), ev()
-        a.record()
-        bd.bd_confidence_commit(lg1[i % n_copies_lg], tok1, msk1, sw.block_size, sw.threshold, want_rows=False,
-                                workspace=cws1)
-        b_.record()
-        if i >= 10:
-            com_events.append((a, b_))
-    torch.cuda.synchronize()
-    dec1_us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in dec_events])
-    com1_us = np.array([a.elapsed_time(b_) * 1e3 for a, b_ in com_events])
+    dec1_us, com1_us = [], []
+    for rnd in range(4):
+        t_us = primed([lambda i=i: bd.bd_attn_decode_block(qb1, kb1, vb1, kc1[i], vc1[i], ps1, pl1, sw.prefix_len,
+                                                           o=o1, lse=lse1, workspace=ws1)
+                       for i in range(n_copies_kv)])
+        if rnd:
+            dec1_us.extend(t_us)
+        for m in msk1:
+            m.copy_(msk_src)
+        t_us = primed([lambda i=i: bd.bd_confidence_commit(lg1[i], tok1, msk1[i], sw.block_size, sw.threshold,
+                                                           want_rows=False, workspace=cws1)
+                       for i in range(n_copies_lg)])
+        if rnd:
+            com1_us.extend(t_us)
+    dec1_us, com1_us = np.array(dec1_us), np.array(com1_us)
     dec1_bytes = (sw.prefix_len + sw.block_size) * Hkv * D * 2 * 2
     com1_bytes = sw.block_size * sw.vocab * 2
 
@@ -279,8 +300,10 @@ def main():
         "bwd": ({"TFLOPs_2.5x": round(bwd_flops / (np.mean(bwd_ms) * 1e-3) / 1e12, 2),
                  "ms_mean": round(float(np.mean(bwd_ms)), 4)} if have_bwd else None),
         "decode_loop": {"kv_GB_per_step": round(kv_bytes_loop / 1e9, 3),
-                        "attn_ms_mean": round(float(np.mean(dec_ms)), 4),
-                        "attn_GBps": round(kv_bytes_loop / (np.mean(dec_ms) * 1e-3) / 1e9, 1),
+                        "attn_us_median": round(float(np.median(dec_ms)) * 1e3, 1),
+                        "attn_GBps": round(kv_bytes_loop / (np.median(dec_ms) * 1e-3) / 1e9, 1),
+                        "commit_GBps_first_step": round(com_gbs_loop[0], 1),
+                        "commit_GBps_median": round(float(np.median(com_gbs_loop)), 1),
                         "by_threshold": loops},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),
@@ -295,8 +318,8 @@ def main():
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The oracle forward on a bounded sample of the same workload: one (batch, head) pair,
-    query blocks taken from the end of the sequence until the time budget is spent."""
+    """The oracle forward on a bounded sample of the same workload: whole (batch, head)
+    pairs of the 16384-token workload, one after another until the time budget is spent."""
     import workloads as W
     from oracle import attention as OA
     try:
@@ -306,23 +329,23 @@ def cpu_baseline(wl, budget_s: float):
         threads = os.cpu_count()
     rng = np.random.default_rng(wl.seed)
     L, D, blk = wl.seqlen, wl.head_dim, wl.block_size
-    q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
-    k = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
-    v = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((1, L, 1, D), dtype=np.float32))).astype(np.float64)
-    nblk = L // blk
-    done_flops, blocks = 0.0, 0
-    t0 = time.perf_counter()
-    b = nblk - 1
-    while b >= 0 and (time.perf_counter() - t0 < budget_s or blocks < 4):
-        OA.attn_fwd(q, k, v, blk, q_blocks=[b])
-        done_flops += 4.0 * D * blk * min(L, (b + 1) * blk)
-        blocks += 1
-        b -= 1
-    dt = time.perf_counter() - t0
-    return {"value": round(done_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"numpy fp64 oracle forward, 1 of {wl.batch * wl.n_q_heads} (batch, head) pairs, "
-                      f"last {blocks} of {nblk} query blocks of the {L}-token workload ({done_flops / 1e9:.1f} "
-                      f"GFLOP in {dt:.1f} s)"}
+
+    def draw():
+        x = rng.standard_normal((1, L, 1, D), dtype=np.float32)
+        return W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
+    flops_pair = OA.attn_flops(L, blk, 1, D)
+    done, pairs = 0.0, 0
+    t_work = 0.0
+    while pairs < wl.batch * wl.n_q_heads and (t_work < budget_s or pairs == 0):
+        q, k, v = draw(), draw(), draw()
+        t0 = time.perf_counter()
+        OA.attn_fwd(q, k, v, blk)
+        t_work += time.perf_counter() - t0
+        done += flops_pair
+        pairs += 1
+    return {"value": round(done / t_work / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 oracle forward over {pairs} of the {wl.batch * wl.n_q_heads} (batch, head) "
+                      f"pairs of the {L}-token workload ({done / 1e9:.0f} GFLOP in {t_work:.1f} s)"}
 
 
 if __name__ == "__main__":

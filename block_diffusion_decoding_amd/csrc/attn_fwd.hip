@@ -15,13 +15,21 @@
 //
 // Per wave and key tile (S^T formulation, see bd_device.hpp for layouts):
 //   S^T[64 keys x 32 q] = K Q^T   (2 x 8 MFMA 32x32x16; Q^T stays in registers,
-//                                   K rows come from LDS in sigma32 order)
+//                                   K rows are read from LDS in sigma32 order)
 //   online softmax per query column (one cross-lane exchange per tile)
 //   O^T[128 d x 32 q] += V^T P^T   (4 x 4 MFMA 32x32x16; P^T comes straight
-//                                   from the S^T accumulator, V^T from LDS)
-// K and V tiles are staged global -> registers -> LDS, double buffered, with
-// the next tile's global loads in flight during the current tile's MFMAs.  V is
-// written to LDS transposed ([d][key]) so its A operand is one 16-byte read.
+//                                   from the S^T accumulator, V^T is read from
+//                                   the row-major V tile with transposed LDS
+//                                   reads)
+// K and V tiles go global -> LDS directly (no register staging) into an
+// NS-deep ring of swizzled tiles, so NS-1 tiles of loads are in flight while a
+// tile is multiplied; one barrier per tile.
+//
+// Softmax: the score scale is folded into the exponent (one FMA per score
+// before exp2), and the running maximum used as the exponent offset is only
+// raised -- with the matching rescale of O and of the row sum -- when a
+// column's maximum grows by more than 2^8; exact either way, since O and the
+// row sum always share the same offset.
 //
 // Workgroups of one (batch, kv head) are handed to the same XCD (L2 reuse of
 // K/V) and the most expensive query tiles are dispatched first.
@@ -34,14 +42,14 @@ namespace bd {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 64;                       // keys per tile
-constexpr int KP = D + 8;                    // LDS pitch of a K row (elements)
-constexpr int VP = KT + 8;                   // LDS pitch of a V^T row (elements)
-constexpr int K_TILE = KT * KP;              // elements
-constexpr int V_TILE = D * VP;
-constexpr int kNW = 4;                       // waves per workgroup
+constexpr int KT = 64;                    // keys per tile
+constexpr int kNW = 8;                    // waves per workgroup
+constexpr int kNS = 3;                    // LDS ring depth (tiles)
 constexpr int kThreads = kNW * 64;
-constexpr size_t kSmemBytes = 2 * (K_TILE + V_TILE) * sizeof(uint16_t);
+constexpr int kTileBytes = KT * D * 2;    // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr size_t kSmemBytes = (size_t)kNS * kStageBytes;
+constexpr float kRescaleSlack = 8.0f;     // log2 units
 
 struct FwdParams {
   const uint16_t* q;
@@ -53,71 +61,22 @@ struct FwdParams {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-// One tile of K (row layout) and V (transposed) in flight, per thread.
-struct TileRegs {
-  static constexpr int KCH = (KT * D / 8) / kThreads;         // 16-byte K chunks / thread
-  static constexpr int VTASK = (KT / 4) * (D / 8);            // (4 keys x 8 d) tasks per tile
-  static constexpr int VPT = (VTASK + kThreads - 1) / kThreads;
-  uint4 k[KCH];
-  uint4 v[VPT][4];
-};
-
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* kb, const uint16_t* vb, int64_t rs,
-                                          int key0, int kend, int tid) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < TileRegs::KCH; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = key0 + (c >> 4);
-    r.k[i] = key < kend ? ldg16(kb + key * rs + (c & 15) * 8) : z;
-  }
-#pragma unroll
-  for (int i = 0; i < TileRegs::VPT; ++i) {
-    const int task = tid + i * kThreads;
-    const int kq = task & 15, ch = task >> 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = key0 + kq * 4 + e;
-      r.v[i][e] = (task < TileRegs::VTASK && key < kend) ? ldg16(vb + key * rs + ch * 8) : z;
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vt, int tid) {
-#pragma unroll
-  for (int i = 0; i < TileRegs::KCH; ++i) {
-    const int c = tid + i * kThreads;
-    *reinterpret_cast<uint4*>(ks + (c >> 4) * KP + (c & 15) * 8) = r.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < TileRegs::VPT; ++i) {
-    const int task = tid + i * kThreads;
-    if (task >= TileRegs::VTASK) continue;
-    const int kq = task & 15, ch = task >> 4;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[i][0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[i][1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[i][2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[i][3]);
-    uint16_t* dst = vt + (ch * 8) * VP + kq * 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint2 lo = make_uint2(lo_pair(w0[e], w1[e]), lo_pair(w2[e], w3[e]));  // d = 8ch + 2e
-      uint2 hi = make_uint2(hi_pair(w0[e], w1[e]), hi_pair(w2[e], w3[e]));  // d = 8ch + 2e + 1
-      *reinterpret_cast<uint2*>(dst + (2 * e) * VP) = lo;
-      *reinterpret_cast<uint2*>(dst + (2 * e + 1) * VP) = hi;
-    }
+template <int NW, int NS>
+__device__ __forceinline__ void wait_tile(int pending_tiles) {
+  constexpr int per_tile = 2 * (16 / NW);
+  if (NS >= 3 && pending_tiles >= 1) {
+    vm_wait<per_tile * (NS - 2)>();
+  } else {
+    vm_wait<0>();
   }
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* ks = smem;               // [2][KT][KP]
-  uint16_t* vt = smem + 2 * K_TILE;  // [2][D][VP]
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = p.qtiles * p.G;
   const int grp = wid / per_group;
@@ -144,6 +103,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
 
+  // prologue: the first NS-1 tiles in flight
+#pragma unroll
+  for (int s = 0; s < kNS - 1; ++s) {
+    if (s < ntiles) {
+      tile_dma<kNW>(lds0 + s * kStageBytes, kb, kv_rs, s * KT, kend_wg, wave, lane);
+      tile_dma<kNW>(lds0 + s * kStageBytes + kTileBytes, vb, kv_rs, s * KT, kend_wg, wave, lane);
+    }
+  }
+
   bf16x8 qreg[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -151,86 +119,92 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
     if (qrow < L) u = ldg16(qb + qrow * q_rs + 16 * t + 8 * half);
     qreg[t] = as_bf16x8(u);
   }
+  vm_wait<0>();
 
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  float m_use = kNegInf, l_run = 0.f;
+  const float c2 = p.scale_log2;
 
-  TileRegs regs;
-  load_tile(regs, kb, vb, kv_rs, 0, kend_wg, tid);
-  store_tile(regs, ks, vt, tid);
-  __syncthreads();
-
-  const int krow_off = sigma32(col) * KP + 8 * half;
-  const int vrow_off = col * VP + 8 * half;
+  // per-lane LDS offsets of the K A-operand rows (sigma32 order, swizzled)
+  const int krow = sigma32(col);
+  const int kswz = tile_swz(krow);
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(regs, kb, vb, kv_rs, (t + 1) * KT, kend_wg, tid);
+    wait_tile<kNW, kNS>(ntiles - 1 - t);
+    __syncthreads();
+    if (t + kNS - 1 < ntiles) {
+      const uint32_t st = lds0 + ((t + kNS - 1) % kNS) * kStageBytes;
+      tile_dma<kNW>(st, kb, kv_rs, (t + kNS - 1) * KT, kend_wg, wave, lane);
+      tile_dma<kNW>(st + kTileBytes, vb, kv_rs, (t + kNS - 1) * KT, kend_wg, wave, lane);
+    }
     const int key0 = t * KT;
-    if (active && key0 < kend_hi) {
-      const uint16_t* K = ks + buf * K_TILE;
-      const uint16_t* V = vt + buf * V_TILE;
-      f32x16 sacc[2];
+    if (!active || key0 >= kend_hi) continue;
+    const uint32_t Kt = lds0 + (t % kNS) * kStageBytes;
+    const uint32_t Vt = Kt + kTileBytes;
+
+    f32x16 sacc[2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[h2][i] = 0.f;
-        const uint16_t* kr = K + h2 * 32 * KP + krow_off;
+      for (int i = 0; i < 16; ++i) sacc[h2][i] = 0.f;
+      const uint32_t rbase = Kt + (32 * h2 + krow) * 256;
 #pragma unroll
-        for (int ds = 0; ds < 8; ++ds)
-          sacc[h2] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * ds), qreg[ds], sacc[h2]);
-      }
-      const bool partial = key0 + KT > kend_lo;
-      float mx = kNegInf;
+      for (int ds = 0; ds < 8; ++ds)
+        sacc[h2] = mfma_32x32x16(lds_read_b128(rbase + (((2 * ds + half) ^ kswz) << 4)), qreg[ds], sacc[h2]);
+    }
+    // entry i of block h2 holds key key0 + 32*h2 + 16*(i/8) + 8*half + (i%8)
+    float mx = kNegInf;
+    if (key0 + KT > kend_lo) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float s = sacc[h2][i] * p.scale_log2;
-          if (partial) {
-            const int key = key0 + 32 * h2 + 16 * (i >> 3) + 8 * half + (i & 7);
-            if (key >= kq) s = kNegInf;
-          }
-          sacc[h2][i] = s;
-          mx = fmaxf(mx, s);
+          const int key = key0 + 32 * h2 + 16 * (i >> 3) + 8 * half + (i & 7);
+          if (key >= kq) sacc[h2][i] = kNegInf;
+          mx = fmaxf(mx, sacc[h2][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);
-      float psum = 0.f;
-      bf16x8 pb[4];
+    } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pv[e] = exp2_fast(sacc[h2][8 * j + e] - m_new);
-            psum += pv[e];
-          }
-          pb[2 * h2 + j] = pack_bf16x8(pv);
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[h2][i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    const bool grow = mx > m_use + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_use;
+      const float alpha = exp2_fast(m_use - m_new);
+      m_use = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vr = V + db * 32 * VP + vrow_off;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          oacc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vr + 16 * s4), pb[s4], oacc[db]);
-      }
     }
-    if (t + 1 < ntiles) store_tile(regs, ks + (buf ^ 1) * K_TILE, vt + (buf ^ 1) * V_TILE, tid);
-    __syncthreads();
+    const float nm = -m_use;
+    float psum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = exp2_fast(__builtin_fmaf(sacc[h2][8 * j + e], c2, nm));
+          psum += pv[e];
+        }
+        pb[2 * h2 + j] = pack_bf16x8(pv);
+      }
+    l_run += psum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) oacc[db] = mfma_32x32x16(tile_read_t(Vt, db, s4, lane), pb[s4], oacc[db]);
   }
 
   if (!active) return;
@@ -246,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
                            pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv));
       *reinterpret_cast<uint2*>(orow + 32 * db + 8 * j + 4 * half) = w;
     }
-  if (p.lse && half == 0) p.lse[((int64_t)b * p.Hq + hq) * L + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  if (p.lse && half == 0) p.lse[((int64_t)b * p.Hq + hq) * L + qrow] = (m_use + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace

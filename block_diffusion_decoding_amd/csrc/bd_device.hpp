@@ -94,4 +94,90 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
 }
 
+
+// ---------------------------------------------------------------------------
+// 64-row x 128-column bf16 tiles in LDS (256-byte rows, no padding).  The 16
+// byte chunks of row r are XOR-swizzled: logical chunk c sits at physical
+// chunk c ^ tile_swz(r).  With this layout
+//   * a 16-byte A-operand read of 16 distinct rows (any rows whose low four
+//     bits differ) at one logical chunk touches all 64 banks once, and
+//   * a transposed read (ds_read_b64_tr_b16) of 4 consecutive rows by 16
+//     lanes touches 8 distinct chunks,
+// so neither access pattern has bank conflicts.
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r * 256 + ((c ^ tile_swz(r)) << 4)); }
+
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l of
+// the wave writes bytes [lds_base + 16 l, +16).  Issued through inline asm so
+// that the compiler does not fence every later LDS read on it; the caller
+// waits with vm_wait<N>() before a barrier.  M0 is restored afterwards.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Copy this wave's share of a 64-row tile (rows row0 .. row0+63 of a row-major
+// bf16 matrix with row stride `rs` elements; rows >= nrows are clamped to the
+// last valid row) into the swizzled LDS tile at byte address `lds_tile`.
+// The tile is 16 wave-instructions of 1 KB (4 rows each); wave w of NW issues
+// instructions w*16/NW .. +16/NW-1.
+template <int NW>
+__device__ __forceinline__ void tile_dma(uint32_t lds_tile, const uint16_t* g, int64_t rs, int row0, int nrows,
+                                         int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int n = wave * (16 / NW) + i;
+    const int r = 4 * n + (lane >> 4);
+    const int c = (lane & 15) ^ tile_swz(r);
+    const int row = min(row0 + r, nrows - 1);
+    lds_dma16(g + row * rs + 8 * c, lds_tile + n * 1024);
+  }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes 4j + i / 4, j = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(uint32_t lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>((uintptr_t)lds_addr));
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t lds_addr) {
+  return *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>((uintptr_t)lds_addr);
+}
+
+// A operand (rows = head dim, k = 16 tile rows 16*s .. 16*s+15) of a 32x32x16
+// product, read transposed from a row-major swizzled tile T[row][d]: lane l
+// gets T[16s + 8(l/32) + r][32 db + l % 32] for r = 0..7.
+__device__ __forceinline__ bf16x8 tile_read_t(uint32_t lds_tile, int db, int s, int lane) {
+  const int li = lane & 15;
+  const int half = lane >> 5;
+  const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((li & 3) >> 1);
+  i16x4 v[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 16 * s + 8 * half + 4 * t + (li >> 2);
+    v[t] = lds_read_tr16(lds_tile + tile_off(row, c) + 8 * (li & 1));
+  }
+  i16x4 lo = v[0], hi = v[1];
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 }  // namespace bd
