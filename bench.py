@@ -41,11 +41,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run each hot-path kernel a few times plus a 1 GiB reference copy (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize", nargs="+", metavar="DB",
+                    help="summarize rocprofv3 result databases into a text profile (see --out, --title)")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="", help="the command that produced the databases (recorded)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the block-causal attention, decode and commit kernels "
               "shard without communication (see the design notes); run it with --gpus 1.", file=sys.stderr)
@@ -126,6 +136,28 @@ def main():
     kv_bytes_loop = float((plen.astype(np.int64) + lw.block_size).sum() * Hkv * D * 2 * 2)
     T_step = 0.95
     loop_state = {"step": 0}
+
+    if args.traffic_probe:
+        # Counter runs (rocprofv3 --pmc) read per-dispatch HBM bytes of these kernels; a
+        # plain 1 GiB device copy gives the scale of each counter.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
+        for _ in range(3):
+            bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
+        if have_bwd:
+            for _ in range(2):
+                bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+        for i in range(3):
+            masked.fill_(1)
+            bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
+            bd.bd_confidence_commit(logit_pool[i % n_pool], tokens, masked, lw.block_size, T_step, conf=conf,
+                                    pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+        torch.cuda.synchronize()
+        print("traffic probe done", flush=True)
+        return
 
     def one_step(rec):
         """decode + commit for every sequence, then forward + backward; one sync at the end."""
@@ -291,7 +323,8 @@ def main():
                    "block_size": blk, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
                    "decode_seqs": lw.n_seq, "vocab": V},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("attn_fwd_bf16_d128"), "traffic_unit": "HBM bytes per launch",
                      "kernel": "attn_fwd_bf16_d128", "flops_per_launch": fwd_flops,
                      "avg_launch_ms": round(fwd_avg, 4)},
         "cpu_baseline": cpu,
@@ -315,6 +348,90 @@ def main():
                              "GBps": round(com1_bytes / (np.median(com1_us) * 1e-6) / 1e9, 1)},
     }
     print(json.dumps(line), flush=True)
+
+
+KERNEL_SRC = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of every kernel source: counter profiles are valid only for the sources they ran."""
+    import hashlib
+    h = hashlib.sha1()
+    for name in sorted(os.listdir(KERNEL_SRC)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes (read + written) per launch of `kernel` from the committed counter profile, or None
+    if there is none for the current kernel sources."""
+    path = os.path.join(PROFILES, "hbm_traffic_hot_path_kernels.txt")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash()
+    for ln in open(path):
+        parts = ln.split()
+        if len(parts) >= 5 and parts[0] == "traffic" and parts[1] == kernel and parts[4] == f"src={want}":
+            return int(float(parts[2]) + float(parts[3]))
+    return None
+
+
+def _short(name: str) -> str:
+    n = name
+    for pre in ("void ", "bd::(anonymous namespace)::", "at::native::(anonymous namespace)::", "at::native::"):
+        n = n.replace(pre, "")
+    return n.split("(")[0].replace(" ", "")[:60]
+
+
+def summarize(args):
+    """Write a short text summary of rocprofv3 result databases (kernel trace or counters)."""
+    import sqlite3
+    out = [f"# {args.title}".rstrip(), f"# command: {args.command}", f"# kernel sources: src={kernel_source_hash()}", ""]
+    pmc = {}
+    for dbp in args.summarize:
+        db = sqlite3.connect(dbp)
+        cur = db.cursor()
+        rows = cur.execute("select count(*) from counters_collection").fetchone()[0]
+        if rows:
+            for kname, cname, n, avg in cur.execute(
+                    "select kernel_name, counter_name, count(*), avg(value) from counters_collection "
+                    "group by kernel_name, counter_name"):
+                pmc.setdefault(_short(kname), {})[cname] = (n, avg)
+        else:
+            out.append(f"## kernel trace: {os.path.basename(dbp)}")
+            out.append(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s}")
+            for kname, n, avg, mn, mx, tot in cur.execute(
+                    "select name, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
+                    "from kernels group by name order by sum(end-start) desc limit 25"):
+                out.append(f"{_short(kname):60s} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} "
+                           f"{tot / 1e6:10.3f}")
+            out.append("")
+    if pmc:
+        names = sorted({c for d in pmc.values() for c in d})
+        out.append("## counters (average per dispatch)")
+        out.append(f"{'kernel':60s} " + " ".join(f"{c:>26s}" for c in names))
+        for kname, d in sorted(pmc.items()):
+            out.append(f"{kname:60s} " + " ".join(f"{d[c][1]:26.6g}" if c in d else f"{'-':>26s}" for c in names))
+        copy = next((d for k, d in pmc.items() if "copyBuffer" in k), None)
+        if copy and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
+            gib_kib = float(1 << 20)
+            ff, fw = gib_kib / copy["FETCH_SIZE"][1], gib_kib / copy["WRITE_SIZE"][1]
+            out.append("")
+            out.append(f"## HBM bytes per launch; counter scale from the 1 GiB reference copy: FETCH x{ff:.3f}, "
+                       f"WRITE x{fw:.3f}")
+            out.append("# traffic <kernel> <read_bytes> <written_bytes> src=<kernel source hash>")
+            for kname, d in sorted(pmc.items()):
+                if "FETCH_SIZE" in d and "WRITE_SIZE" in d and "copyBuffer" not in kname:
+                    out.append(f"traffic {kname} {d['FETCH_SIZE'][1] * 1024 * ff:.0f} {d['WRITE_SIZE'][1] * 1024 * fw:.0f} "
+                               f"src={kernel_source_hash()}")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def cpu_baseline(wl, budget_s: float):

@@ -8,7 +8,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbd.so")
+# BD_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("BD_LIBRARY") or os.path.join(_HERE, "libbd.so")
 
 BD_OK, BD_ERR_NULL, BD_ERR_SHAPE, BD_ERR_UNSUPPORTED, BD_ERR_WORKSPACE, BD_ERR_VALUE, BD_ERR_HIP, \
     BD_ERR_ALIGNMENT = range(8)

@@ -29,9 +29,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 SOURCES = ["bd_api.cpp", "commit.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str, defines: dict) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *[f"-D{k}={v}" for k, v in defines.items()], "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,20 +43,29 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link libbd.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines: dict | None = None, lib_path: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile all sources and link the library; returns its path.
+
+    ``defines`` overrides the compile-time pipeline shapes (BD_FWD_NW, BD_FWD_NS,
+    BD_DECODE_NS, BD_DECODE_TARGET_WGS); with ``lib_path`` the result is written
+    elsewhere instead of replacing the package's libbd.so.
+    """
+    defines = dict(defines or {})
+    build_dir = build_dir or BUILD
+    lib_path = lib_path or LIB
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -7,14 +7,17 @@
 //   decode_split  one workgroup per (sequence, kv head, row tile of 64 query
 //                 rows = block tokens x the query heads of the group, key
 //                 split).  Four waves own 16 query rows each and share K/V
-//                 tiles of 64 keys staged global -> LDS (V transposed), double
-//                 buffered.  Per tile and wave:
-//                   S^T[64 keys x 16 q] = K Q^T  (4 x 4 MFMA 16x16x32)
-//                   O^T[128 d x 16 q]  += V^T P^T (8 x 2 MFMA 16x16x32)
+//                 tiles of 32 keys copied global -> LDS directly into a ring of
+//                 kNS swizzled stages (kNS-1 tiles of loads in flight; 48 KB of
+//                 LDS, so three workgroups share a CU).  Per tile and wave:
+//                   S^T[32 keys x 16 q] = K Q^T  (2 x 4 MFMA 16x16x32)
+//                   O^T[128 d x 16 q]  += V^T P^T (8 MFMA 16x16x32, V^T read
+//                                                  transposed from LDS)
 //                 and writes its unnormalised partial (m, l, acc) in fp32.
-//   decode_merge  one workgroup per (sequence, kv head, row tile) combines the
-//                 splits exactly: m = max m_s, l = sum l_s 2^(m_s - m),
-//                 O = sum acc_s 2^(m_s - m) / l, and writes O (bf16) and LSE.
+//   decode_merge  combines the splits exactly: m = max m_s,
+//                 l = sum l_s 2^(m_s - m), O = sum acc_s 2^(m_s - m) / l, and
+//                 writes O (bf16) and LSE; 128 threads per query row, one per
+//                 head-dim entry.
 // Each K/V byte of the cache is read from HBM once per step.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
@@ -22,18 +25,28 @@
 #include <algorithm>
 #include <mutex>
 
+// Pipeline shape (compile-time): LDS ring depth and the workgroup count the
+// split plan aims for.
+#ifndef BD_DECODE_NS
+#define BD_DECODE_NS 3
+#endif
+#ifndef BD_DECODE_TARGET_WGS
+#define BD_DECODE_TARGET_WGS 4096
+#endif
+
 namespace bd {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 64;
-constexpr int KP = D + 8;
-constexpr int VP = KT + 8;
-constexpr int K_TILE = KT * KP;
-constexpr int V_TILE = D * VP;
-constexpr int kThreads = 256;
+constexpr int KT = 32;
+constexpr int kNW = 4;
+constexpr int kNS = BD_DECODE_NS;
+constexpr int kThreads = kNW * 64;
 constexpr int kRows = 64;                     // query rows per workgroup (4 waves x 16)
-constexpr size_t kSmemBytes = 2 * (K_TILE + V_TILE) * sizeof(uint16_t);
+constexpr int kTileBytes = KT * D * 2;      // 8 KB
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr size_t kSmemBytes = (size_t)kNS * kStageBytes;
+constexpr int kMergeRows = 2;                 // query rows per merge workgroup
 
 struct DecParams {
   const uint16_t* q_blk;
@@ -51,68 +64,39 @@ struct DecParams {
   float scale_log2;
 };
 
-__device__ __forceinline__ const uint16_t* key_ptr(const DecParams& p, const uint16_t* cache,
-                                                   const uint16_t* blk, int64_t start, int P, int n,
-                                                   int kvh, int j) {
-  const int64_t rs = (int64_t)p.Hkv * D;
-  return j < P ? cache + (start + j) * rs + kvh * D
-               : blk + ((int64_t)n * p.blk_len + (j - P)) * rs + kvh * D;
-}
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-struct DecTileRegs {
-  uint4 k[4];      // 4 chunks of 16 bytes of K
-  uint4 v[4];      // 4 keys x 8 d of V
-};
-
-__device__ __forceinline__ void dec_load(DecTileRegs& r, const DecParams& p, int64_t start, int P, int n,
-                                         int kvh, int key0, int kend, int tid) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
+// Copy this wave's share of the 32-key tile starting at key `key0` of the
+// sequence's key list (prefix rows of the cache, then the block's own rows) into
+// the swizzled LDS tile.  Keys >= kend are clamped to kend - 1.
+__device__ __forceinline__ void dec_tile_dma(uint32_t lds_tile, const uint16_t* cache, const uint16_t* blk,
+                                             int64_t start, int P, int n, int kvh, int blk_len, int Hkv,
+                                             int key0, int kend, int wave, int lane) {
+  const int64_t rs = (int64_t)Hkv * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = key0 + (c >> 4);
-    r.k[i] = key < kend ? ldg16(key_ptr(p, p.k_cache, p.k_blk, start, P, n, kvh, key) + (c & 15) * 8) : z;
-  }
-  const int kq = tid & 15, ch = tid >> 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int key = key0 + kq * 4 + e;
-    r.v[e] = key < kend ? ldg16(key_ptr(p, p.v_cache, p.v_blk, start, P, n, kvh, key) + ch * 8) : z;
-  }
-}
-
-__device__ __forceinline__ void dec_store(const DecTileRegs& r, uint16_t* ks, uint16_t* vt, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * kThreads;
-    *reinterpret_cast<uint4*>(ks + (c >> 4) * KP + (c & 15) * 8) = r.k[i];
-  }
-  const int kq = tid & 15, ch = tid >> 4;
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
-  uint16_t* dst = vt + (ch * 8) * VP + kq * 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    *reinterpret_cast<uint2*>(dst + (2 * e) * VP) = make_uint2(lo_pair(w0[e], w1[e]), lo_pair(w2[e], w3[e]));
-    *reinterpret_cast<uint2*>(dst + (2 * e + 1) * VP) = make_uint2(hi_pair(w0[e], w1[e]), hi_pair(w2[e], w3[e]));
+  for (int i = 0; i < KT / 4 / kNW; ++i) {
+    const int nn = wave * (KT / 4 / kNW) + i;
+    const int r = 4 * nn + (lane >> 4);
+    const int c = (lane & 15) ^ tile_swz(r);
+    const int j = min(key0 + r, kend - 1);
+    const uint16_t* src = j < P ? cache + (start + j) * rs : blk + ((int64_t)n * blk_len + (j - P)) * rs;
+    lds_dma16(src + kvh * D + 8 * c, lds_tile + nn * 1024);
   }
 }
 
 __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* ks = smem;
-  uint16_t* vt = smem + 2 * K_TILE;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  const int split = blockIdx.x % p.nsplit;
-  const int unit = blockIdx.x / p.nsplit;
-  const int rt = unit % p.row_tiles;
-  const int nk = unit / p.row_tiles;
-  const int kvh = nk % p.Hkv, n = nk / p.Hkv;
+  // Workgroup order: kv head fastest, then row tile, then split, then sequence.
+  // A cache row interleaves the kv heads, so the workgroups dispatched together
+  // fetch neighbouring pieces of the same rows.
+  int bid = blockIdx.x;
+  const int kvh = bid % p.Hkv;
+  bid /= p.Hkv;
+  const int rt = bid % p.row_tiles;
+  bid /= p.row_tiles;
+  const int split = bid % p.nsplit;
+  const int n = bid / p.nsplit;
+  const int unit = (n * p.Hkv + kvh) * p.row_tiles + rt;
 
   const int P = p.prefix_len[n];
   const int64_t start = p.prefix_start[n];
@@ -122,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   const int k1 = min(total, k0 + p.chunk);
   const int ntiles = (k1 - k0 + KT - 1) / KT;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4;
   const int rloc = wave * 16 + col;            // row within the tile
   const int r = rt * kRows + rloc;             // row within the unit: r = hl * blk_len + t
@@ -130,149 +115,166 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   const int hl = rvalid ? r / p.blk_len : 0, tok = rvalid ? r % p.blk_len : 0;
   const int hq = kvh * p.G + hl;
 
+#pragma unroll
+  for (int s = 0; s < kNS - 1; ++s) {
+    if (s < ntiles) {
+      const uint32_t st = lds0 + s * kStageBytes;
+      dec_tile_dma(st, p.k_cache, p.k_blk, start, P, n, kvh, p.blk_len, p.Hkv, k0 + s * KT, k1, wave, lane);
+      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, start, P, n, kvh, p.blk_len, p.Hkv, k0 + s * KT, k1, wave,
+                   lane);
+    }
+  }
+
   bf16x8 qreg[4];
   {
     const uint16_t* qr = p.q_blk + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + 8 * g4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) qreg[t] = as_bf16x8(rvalid ? ldg16(qr + 32 * t) : make_uint4(0, 0, 0, 0));
   }
+  vm_wait<0>();
 
   f32x4 oacc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_use = kNegInf, l_run = 0.f;
+  const float c2 = p.scale_log2;
 
-  DecTileRegs regs;
-  dec_load(regs, p, start, P, n, kvh, k0, k1, tid);
-  dec_store(regs, ks, vt, tid);
-  __syncthreads();
-
-  // A-operand row of 16-key block kb for lane row rho = col:
-  //   key 32*(kb/2) + 8*(rho/4) + 4*(kb%2) + rho%4
+  // A-operand row of 16-key block kb (0, 1) for lane row rho = col:
+  //   key 8*(rho/4) + 4*kb + rho%4
   // so that accumulator entry i of lane (col, g4) in block kb holds key
-  //   32*(kb/2) + 8*g4 + 4*(kb%2) + i,
-  // the B-operand k-slice of the PV product over keys 32*(kb/2) .. +31.
+  //   8*g4 + 4*kb + i,
+  // the B-operand k-slice of the PV product over the tile's 32 keys.
   const int arow = 8 * (col >> 2) + (col & 3);
+  constexpr int per_tile = 2 * (KT / 4 / kNW);
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+    const int pending = min(kNS - 2, ntiles - 1 - t);
+    if (pending >= 3) vm_wait<3 * per_tile>();
+    else if (pending == 2) vm_wait<2 * per_tile>();
+    else if (pending == 1) vm_wait<per_tile>();
+    else vm_wait<0>();
+    __syncthreads();
+    if (t + kNS - 1 < ntiles) {
+      const uint32_t st = lds0 + ((t + kNS - 1) % kNS) * kStageBytes;
+      const int kn = k0 + (t + kNS - 1) * KT;
+      dec_tile_dma(st, p.k_cache, p.k_blk, start, P, n, kvh, p.blk_len, p.Hkv, kn, k1, wave, lane);
+      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, start, P, n, kvh, p.blk_len, p.Hkv, kn, k1, wave, lane);
+    }
     const int key0 = k0 + t * KT;
-    if (t + 1 < ntiles) dec_load(regs, p, start, P, n, kvh, key0 + KT, k1, tid);
-    const uint16_t* K = ks + buf * K_TILE;
-    const uint16_t* V = vt + buf * V_TILE;
+    const uint32_t Kt = lds0 + (t % kNS) * kStageBytes;
+    const uint32_t Vt = Kt + kTileBytes;
 
-    f32x4 sacc[4];
+    f32x4 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = K + (32 * (kb >> 1) + 4 * (kb & 1) + arow) * KP + 8 * g4;
+      const int row = 4 * kb + arow;
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
-        sacc[kb] = mfma_16x16x32(*reinterpret_cast<const bf16x8*>(kr + 32 * ds), qreg[ds], sacc[kb]);
+        sacc[kb] = mfma_16x16x32(lds_read_b128(Kt + tile_off(row, 4 * ds + g4)), qreg[ds], sacc[kb]);
     }
-    const bool partial = key0 + KT > k1;
     float mx = kNegInf;
+    if (key0 + KT > k1) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float s = sacc[kb][i] * p.scale_log2;
-        if (partial) {
-          const int key = key0 + 32 * (kb >> 1) + 8 * g4 + 4 * (kb & 1) + i;
-          if (key >= k1) s = kNegInf;
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 8 * g4 + 4 * kb + i;
+          if (key >= k1) sacc[kb][i] = kNegInf;
+          mx = fmaxf(mx, sacc[kb][i]);
         }
-        sacc[kb][i] = s;
-        mx = fmaxf(mx, s);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast(m_run - m_new);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    const bool grow = mx > m_use + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_use;
+      const float alpha = exp2_fast(m_use - m_new);
+      m_use = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+    }
+    const float nm = -m_use;
     float psum = 0.f;
-    bf16x8 pb[2];
+    float pv[8];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = exp2_fast(sacc[2 * s2][i] - m_new);
-        pv[4 + i] = exp2_fast(sacc[2 * s2 + 1][i] - m_new);
-        psum += pv[i] + pv[4 + i];
-      }
-      pb[s2] = pack_bf16x8(pv);
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = exp2_fast(__builtin_fmaf(sacc[0][i], c2, nm));
+      pv[4 + i] = exp2_fast(__builtin_fmaf(sacc[1][i], c2, nm));
+      psum += pv[i] + pv[4 + i];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    const bf16x8 pb = pack_bf16x8(pv);
+    l_run += psum;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      oacc[db] *= alpha;
-      const uint16_t* vr = V + (16 * db + col) * VP + 8 * g4;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        oacc[db] = mfma_16x16x32(*reinterpret_cast<const bf16x8*>(vr + 32 * s2), pb[s2], oacc[db]);
-    }
-    if (t + 1 < ntiles) dec_store(regs, ks + (buf ^ 1) * K_TILE, vt + (buf ^ 1) * V_TILE, tid);
-    __syncthreads();
+    for (int db = 0; db < 8; ++db) oacc[db] = mfma_16x16x32(tile_read_t16(Vt, db, 0, lane), pb, oacc[db]);
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   const int64_t slot = ((int64_t)unit * p.nsplit + split) * kRows + rloc;
-  if (g4 == 0) p.part_ml[slot] = make_float2(m_run, l_tot);
+  if (g4 == 0) p.part_ml[slot] = make_float2(m_use, l_tot);
   float* acc = p.part_acc + slot * D + 4 * g4;
 #pragma unroll
   for (int db = 0; db < 8; ++db)
     *reinterpret_cast<float4*>(acc + 16 * db) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
 }
 
-// Thread layout: 4 threads per row, 32 head-dim entries each.
-__global__ __launch_bounds__(kThreads) void decode_merge(DecParams p) {
-  const int unit = blockIdx.x;
+// 128 threads per query row, one head-dim entry each; kMergeRows rows per workgroup.
+__global__ __launch_bounds__(128 * kMergeRows) void decode_merge(DecParams p) {
+  const int per_unit = kRows / kMergeRows;
+  const int unit = blockIdx.x / per_unit;
+  const int rloc = (blockIdx.x % per_unit) * kMergeRows + threadIdx.x / D;
+  const int d = threadIdx.x % D;
   const int rt = unit % p.row_tiles;
   const int nk = unit / p.row_tiles;
   const int kvh = nk % p.Hkv, n = nk / p.Hkv;
-  const int total = p.prefix_len[n] + p.blk_len;
-  const int ns = min(p.nsplit, (total + p.chunk - 1) / p.chunk);
-  const int tid = threadIdx.x;
-  const int rloc = tid >> 2, part = tid & 3;
   const int r = rt * kRows + rloc;
   if (r >= p.rows) return;
+  const int total = p.prefix_len[n] + p.blk_len;
+  const int ns = min(p.nsplit, (total + p.chunk - 1) / p.chunk);
   const int hl = r / p.blk_len, tok = r % p.blk_len;
   const int hq = kvh * p.G + hl;
 
   const int64_t base = (int64_t)unit * p.nsplit * kRows + rloc;
+  // Loads of up to kBatch splits are issued together (the split count is small
+  // but each load is a round trip to L2 / HBM).
+  constexpr int kBatch = 8;
   float m = kNegInf;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, p.part_ml[base + (int64_t)s * kRows].x);
-  float l = 0.f;
-  float acc[32];
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    float mb[kBatch];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float2 ml = p.part_ml[base + (int64_t)s * kRows];
-    const float w = exp2_fast(ml.x - m);
-    l += ml.y * w;
-    const float4* src = reinterpret_cast<const float4*>(p.part_acc + (base + (int64_t)s * kRows) * D + part * 32);
+    for (int k = 0; k < kBatch; ++k) mb[k] = (s0 + k < ns) ? p.part_ml[base + (int64_t)(s0 + k) * kRows].x : kNegInf;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 a = src[i];
-      acc[4 * i] += a.x * w;
-      acc[4 * i + 1] += a.y * w;
-      acc[4 * i + 2] += a.z * w;
-      acc[4 * i + 3] += a.w * w;
+    for (int k = 0; k < kBatch; ++k) m = fmaxf(m, mb[k]);
+  }
+  float l = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    float2 ml[kBatch];
+    float a[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t slot = base + (int64_t)(s0 + k) * kRows;
+      const bool ok = s0 + k < ns;
+      ml[k] = ok ? p.part_ml[slot] : make_float2(kNegInf, 0.f);
+      a[k] = ok ? p.part_acc[slot * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = exp2_fast(ml[k].x - m);
+      l += ml[k].y * w;
+      acc += a[k] * w;
     }
   }
-  const float inv = 1.0f / l;
-  uint16_t* orow = p.o + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + part * 32;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 w;
-    w.x = pack_bf16x2(acc[8 * i] * inv, acc[8 * i + 1] * inv);
-    w.y = pack_bf16x2(acc[8 * i + 2] * inv, acc[8 * i + 3] * inv);
-    w.z = pack_bf16x2(acc[8 * i + 4] * inv, acc[8 * i + 5] * inv);
-    w.w = pack_bf16x2(acc[8 * i + 6] * inv, acc[8 * i + 7] * inv);
-    *reinterpret_cast<uint4*>(orow + 8 * i) = w;
-  }
-  if (p.lse && part == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
+  const float o = acc / l;
+  const uint16_t ob = __builtin_bit_cast(uint16_t, (__bf16)o);
+  p.o[(((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + d] = ob;
+  if (p.lse && d == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
 }
 
 struct Plan {
@@ -286,12 +288,11 @@ Plan make_plan(const DecodeShape& s) {
   pl.row_tiles = (rows + kRows - 1) / kRows;
   pl.units = (long long)s.n_seq * s.n_kv_heads * pl.row_tiles;
   const long long total_max = (long long)s.max_prefix_len + s.blk_len;
-  // Aim for about 2048 busy workgroups (8 per CU) while keeping each split at
-  // least two tiles long, so that partial-state traffic stays small next to
-  // the K/V bytes a split streams.
-  const long long want_splits = std::max<long long>(1, (2048 + pl.units - 1) / pl.units);
+  // Aim for about BD_DECODE_TARGET_WGS workgroups over the longest sequence's
+  // splits, with splits of at least four tiles (128 keys).
+  const long long want_splits = std::max<long long>(1, (BD_DECODE_TARGET_WGS + pl.units - 1) / pl.units);
   long long chunk = (total_max + want_splits - 1) / want_splits;
-  chunk = std::max<long long>(2 * KT, ((chunk + KT - 1) / KT) * KT);
+  chunk = std::max<long long>(4 * KT, ((chunk + KT - 1) / KT) * KT);
   pl.chunk = (int)chunk;
   pl.nsplit = (int)((total_max + chunk - 1) / chunk);
   return pl;
@@ -341,7 +342,8 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   hipLaunchKernelGGL(decode_split, dim3((unsigned)(pl.units * pl.nsplit)), dim3(kThreads), kSmemBytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge, dim3((unsigned)pl.units), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)(pl.units * (kRows / kMergeRows))), dim3(128 * kMergeRows), 0, st,
+                     p);
   return hipGetLastError();
 }
 

@@ -21,9 +21,11 @@
 //                                   from the S^T accumulator, V^T is read from
 //                                   the row-major V tile with transposed LDS
 //                                   reads)
-// K and V tiles go global -> LDS directly (no register staging) into an
-// NS-deep ring of swizzled tiles, so NS-1 tiles of loads are in flight while a
-// tile is multiplied; one barrier per tile.
+// K and V tiles go global -> LDS directly (no register staging) into a
+// two-stage ring of swizzled tiles: the next tile's loads are in flight while a
+// tile is multiplied; one barrier per tile.  Every LDS read address is a
+// per-lane register computed once plus a compile-time offset (the tile loop is
+// unrolled by the ring depth).
 //
 // Softmax: the score scale is folded into the exponent (one FMA per score
 // before exp2), and the running maximum used as the exponent offset is only
@@ -37,14 +39,21 @@
 #include "bd_kernels.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace bd {
 namespace {
 
 constexpr int D = 128;
 constexpr int KT = 64;                    // keys per tile
-constexpr int kNW = 8;                    // waves per workgroup
-constexpr int kNS = 3;                    // LDS ring depth (tiles)
+#ifndef BD_FWD_NW
+#define BD_FWD_NW 8
+#endif
+#ifndef BD_FWD_NS
+#define BD_FWD_NS 2
+#endif
+constexpr int kNW = BD_FWD_NW;            // waves per workgroup
+constexpr int kNS = BD_FWD_NS;            // LDS ring depth (tiles)
 constexpr int kThreads = kNW * 64;
 constexpr int kTileBytes = KT * D * 2;    // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;
@@ -60,16 +69,6 @@ struct FwdParams {
   int L, Hq, Hkv, G, blk, qtiles;
   float scale_log2;  // softmax scale * log2(e)
 };
-
-template <int NW, int NS>
-__device__ __forceinline__ void wait_tile(int pending_tiles) {
-  constexpr int per_tile = 2 * (16 / NW);
-  if (NS >= 3 && pending_tiles >= 1) {
-    vm_wait<per_tile * (NS - 2)>();
-  } else {
-    vm_wait<0>();
-  }
-}
 
 __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -103,13 +102,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
 
-  // prologue: the first NS-1 tiles in flight
-#pragma unroll
-  for (int s = 0; s < kNS - 1; ++s) {
-    if (s < ntiles) {
-      tile_dma<kNW>(lds0 + s * kStageBytes, kb, kv_rs, s * KT, kend_wg, wave, lane);
-      tile_dma<kNW>(lds0 + s * kStageBytes + kTileBytes, vb, kv_rs, s * KT, kend_wg, wave, lane);
-    }
+  static_assert(kNS == 2, "the tile loop below is written for a two-stage ring");
+  // prologue: tile 0 in flight
+  if (ntiles > 0) {
+    tile_dma<kNW>(lds0, kb, kv_rs, 0, kend_wg, wave, lane);
+    tile_dma<kNW>(lds0 + kTileBytes, vb, kv_rs, 0, kend_wg, wave, lane);
   }
 
   bf16x8 qreg[8];
@@ -119,7 +116,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
     if (qrow < L) u = ldg16(qb + qrow * q_rs + 16 * t + 8 * half);
     qreg[t] = as_bf16x8(u);
   }
-  vm_wait<0>();
 
   f32x16 oacc[4];
 #pragma unroll
@@ -129,32 +125,50 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   float m_use = kNegInf, l_run = 0.f;
   const float c2 = p.scale_log2;
 
-  // per-lane LDS offsets of the K A-operand rows (sigma32 order, swizzled)
-  const int krow = sigma32(col);
-  const int kswz = tile_swz(krow);
+  // Per-lane LDS byte addresses (stage 0), so that every read below is this
+  // register plus a compile-time offset.
+  //   K A operand, d-step ds: row sigma32(col) (+32 for the second key block),
+  //     logical chunk 2*ds + half.
+  //   V^T A operand (transposed read), d-block db, k-step s4, half-read tt:
+  //     row 16*s4 + 8*half + 4*tt + jj, logical chunk 4*db + 2*g1 + b, where
+  //     jj = (lane%16)/4, g1 = (lane/16)%2, b = (lane%4)/2; with tile_swz the
+  //     physical chunk is 4*(db^jj) + 2*(g1^half) + (b ^ tt ^ (s4%2)).
+  uint32_t kaddr[8], vaddr[4][2];
+  {
+    const int krow = sigma32(col);
+    const int kswz = tile_swz(krow);
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) kaddr[ds] = lds0 + krow * 256 + (((2 * ds + half) ^ kswz) << 4);
+    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        vaddr[db][x] = lds0 + kTileBytes + (8 * half + jj) * 256 +
+                       ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) + 8 * (li & 1);
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_tile<kNW, kNS>(ntiles - 1 - t);
+  auto step = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr uint32_t so = S * kStageBytes;
+    vm_wait<0>();
     __syncthreads();
-    if (t + kNS - 1 < ntiles) {
-      const uint32_t st = lds0 + ((t + kNS - 1) % kNS) * kStageBytes;
-      tile_dma<kNW>(st, kb, kv_rs, (t + kNS - 1) * KT, kend_wg, wave, lane);
-      tile_dma<kNW>(st + kTileBytes, vb, kv_rs, (t + kNS - 1) * KT, kend_wg, wave, lane);
+    if (t + 1 < ntiles) {
+      const uint32_t st = lds0 + (1 - S) * kStageBytes;
+      tile_dma<kNW>(st, kb, kv_rs, (t + 1) * KT, kend_wg, wave, lane);
+      tile_dma<kNW>(st + kTileBytes, vb, kv_rs, (t + 1) * KT, kend_wg, wave, lane);
     }
     const int key0 = t * KT;
-    if (!active || key0 >= kend_hi) continue;
-    const uint32_t Kt = lds0 + (t % kNS) * kStageBytes;
-    const uint32_t Vt = Kt + kTileBytes;
+    if (!active || key0 >= kend_hi) return;
 
     f32x16 sacc[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[h2][i] = 0.f;
-      const uint32_t rbase = Kt + (32 * h2 + krow) * 256;
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds)
-        sacc[h2] = mfma_32x32x16(lds_read_b128(rbase + (((2 * ds + half) ^ kswz) << 4)), qreg[ds], sacc[h2]);
+        sacc[h2] = mfma_32x32x16(lds_read_b128(kaddr[ds] + so + h2 * 32 * 256), qreg[ds], sacc[h2]);
     }
     // entry i of block h2 holds key key0 + 32*h2 + 16*(i/8) + 8*half + (i%8)
     float mx = kNegInf;
@@ -204,7 +218,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) oacc[db] = mfma_32x32x16(tile_read_t(Vt, db, s4, lane), pb[s4], oacc[db]);
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const i16x4 lo = lds_read_tr16(vaddr[db][s4 & 1] + so + (16 * s4) * 256);
+        const i16x4 hi = lds_read_tr16(vaddr[db][(s4 & 1) ^ 1] + so + (16 * s4 + 4) * 256);
+        oacc[db] = mfma_32x32x16(cat_i16x4(lo, hi), pb[s4], oacc[db]);
+      }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>(), t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
   }
 
   if (!active) return;

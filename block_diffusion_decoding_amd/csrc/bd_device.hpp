@@ -37,10 +37,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+// Round to nearest even; one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
@@ -98,13 +101,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // ---------------------------------------------------------------------------
 // 64-row x 128-column bf16 tiles in LDS (256-byte rows, no padding).  The 16
 // byte chunks of row r are XOR-swizzled: logical chunk c sits at physical
-// chunk c ^ tile_swz(r).  With this layout
-//   * a 16-byte A-operand read of 16 distinct rows (any rows whose low four
-//     bits differ) at one logical chunk touches all 64 banks once, and
-//   * a transposed read (ds_read_b64_tr_b16) of 4 consecutive rows by 16
-//     lanes touches 8 distinct chunks,
-// so neither access pattern has bank conflicts.
-__device__ __forceinline__ int tile_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// chunk c ^ tile_swz(r), where tile_swz maps row bits (r0, r1, r3, r2^r4) to
+// chunk bits (2, 3, 1, 0).  This makes each of the access patterns below hit
+// every bank at most once per LDS cycle:
+//   * 16-byte A-operand reads by 16 lanes at one logical chunk, the lanes'
+//     rows covering the 16 values of bits 0-3 (32x32 products), or rows
+//     {0-3, 8-11, 16-19, 24-27} + const (16x16 products);
+//   * transposed 8-byte reads (ds_read_b64_tr_b16) by 32 lanes: 4 consecutive
+//     rows x an aligned block of 4 chunks (32x32 products), or 2 x 4 rows 8
+//     apart x an aligned chunk pair (16x16 products).
+__device__ __forceinline__ int tile_swz(int r) {
+  return ((r & 1) << 2) | (((r >> 1) & 1) << 3) | (((r >> 3) & 1) << 1) | (((r >> 2) ^ (r >> 4)) & 1);
+}
 __device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r * 256 + ((c ^ tile_swz(r)) << 4)); }
 
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l of
@@ -161,23 +169,38 @@ __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t lds_addr) {
   return *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>((uintptr_t)lds_addr);
 }
 
+// Four consecutive rows of one column, read transposed from a row-major
+// swizzled tile T[row][d]: within each 16-lane group, lane i (i = lane % 16)
+// receives T[row0 + j][dbase + i] for j = 0..3 (dbase a multiple of 8; row0
+// and dbase may differ between groups).
+__device__ __forceinline__ i16x4 tile_read_t4(uint32_t lds_tile, int row0, int dbase, int lane) {
+  const int li = lane & 15;
+  const int row = row0 + (li >> 2);
+  const int d = dbase + 4 * (li & 3);
+  return lds_read_tr16(lds_tile + tile_off(row, d >> 3) + 2 * (d & 7));
+}
+
+__device__ __forceinline__ bf16x8 cat_i16x4(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // A operand (rows = head dim, k = 16 tile rows 16*s .. 16*s+15) of a 32x32x16
 // product, read transposed from a row-major swizzled tile T[row][d]: lane l
 // gets T[16s + 8(l/32) + r][32 db + l % 32] for r = 0..7.
 __device__ __forceinline__ bf16x8 tile_read_t(uint32_t lds_tile, int db, int s, int lane) {
-  const int li = lane & 15;
-  const int half = lane >> 5;
-  const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((li & 3) >> 1);
-  i16x4 v[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = 16 * s + 8 * half + 4 * t + (li >> 2);
-    v[t] = lds_read_tr16(lds_tile + tile_off(row, c) + 8 * (li & 1));
-  }
-  i16x4 lo = v[0], hi = v[1];
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
+  const int row0 = 16 * s + 8 * (lane >> 5);
+  const int dbase = 32 * db + 16 * ((lane >> 4) & 1);
+  return cat_i16x4(tile_read_t4(lds_tile, row0, dbase, lane), tile_read_t4(lds_tile, row0 + 4, dbase, lane));
+}
+
+// A operand (rows = head dim, k = 32 tile rows 32*s .. 32*s+31) of a 16x16x32
+// product, read transposed: lane l gets T[32s + 8(l/16) + r][16 db + l % 16]
+// for r = 0..7.
+__device__ __forceinline__ bf16x8 tile_read_t16(uint32_t lds_tile, int db, int s, int lane) {
+  const int row0 = 32 * s + 8 * (lane >> 4);
+  return cat_i16x4(tile_read_t4(lds_tile, row0, 16 * db, lane), tile_read_t4(lds_tile, row0 + 4, 16 * db, lane));
 }
 
 }  // namespace bd
