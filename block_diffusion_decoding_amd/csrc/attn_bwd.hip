@@ -8,87 +8,50 @@
 // i sees key j iff floor(j / L') <= floor(i / L').
 //
 // Three kernels, no atomics (bit-for-bit deterministic):
-//   bwd_dsum  D for every (batch, head, row).
+//   bwd_prep  per (batch, head, row): D = rowsum(dO * O) and LSE * log2(e),
+//             stored interleaved in the workspace.
 //   bwd_dkdv  workgroup = 4 waves = 128 consecutive keys of one (batch, kv
 //             head); each wave owns 32 keys with K and V in registers and walks
-//             the query tiles (64 rows, both layouts staged in LDS) of every
-//             query head of the group, from the first query that can see its
-//             keys to the end of the sequence.  Per 32-query slice:
-//               S  = Q K^T, dP = dO V^T        (A = Q / dO rows from LDS)
-//               dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T from LDS,
-//                                               B = P / dS from the accumulator)
-//             The query rows of the A operand are read in sigma32 order so that
-//             the S and dP accumulators are already in B-operand layout.
-//   bwd_dq    workgroup = 4 waves = 128 query rows of one (batch, q head), as
-//             the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, over the
-//             key tiles its rows can see (K in both layouts and V in LDS).
+//             the query tiles (64 rows) of every query head of the group, from
+//             the first query that can see its keys to the end of the sequence.
+//             Q and dO tiles (and their D / LSE slices) go global -> LDS
+//             directly into a three-stage ring of swizzled row-major tiles.  Per
+//             32-query slice:
+//               S  = Q K^T, dP = dO V^T        (A = Q / dO rows from LDS, in
+//                                               sigma32 order)
+//               dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by transposed
+//                                               LDS reads, B = P / dS straight
+//                                               from the accumulators)
+//   bwd_dq    workgroup = 8 waves = 256 query rows of one (batch, q head), as
+//             the forward: per 32-key half of a 64-key tile,
+//             S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T by transposed
+//             reads of the K tile), over the key tiles its rows can see; K and V
+//             tiles in a two-stage direct-to-LDS ring.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace bd {
 namespace {
 
 constexpr int D = 128;
-constexpr int RP = D + 8;      // pitch of a row-layout tile [rows][D]
-constexpr int TP = 64 + 8;     // pitch of a transposed tile [D][64 rows]
-constexpr int ROW_TILE = 64 * RP;
-constexpr int T_TILE = D * TP;
-constexpr int kThreads = 256;
+constexpr int kTileBytes = 64 * D * 2;   // 16 KB: one 64-row bf16 tile
 
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *dO;
   const float* lse;
-  float* Dsum;
+  float2* dl;          // [B, Hq, L]: (D, LSE * log2 e)
   uint16_t *dq, *dk, *dv;
   int B, L, Hq, Hkv, G, blk;
   float scale, scale_log2;
 };
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-// A 64-row x 128-column bf16 tile in flight: thread t holds rows 4*(t%16)..+3,
-// columns 8*(t/16)..+7 (four 16-byte loads).
-struct Tile64 {
-  uint4 r[4];
-};
-
-template <typename RowPtr>
-__device__ __forceinline__ void tile_load(Tile64& t, const RowPtr& row_ptr, int row0, int nrows, int tid) {
-  const int rq = tid & 15, ch = tid >> 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = row0 + 4 * rq + e;
-    t.r[e] = r < nrows ? ldg16(row_ptr(r) + 8 * ch) : make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void tile_store_rows(const Tile64& t, uint16_t* dst, int tid) {
-  const int rq = tid & 15, ch = tid >> 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(dst + (4 * rq + e) * RP + 8 * ch) = t.r[e];
-}
-
-__device__ __forceinline__ void tile_store_transposed(const Tile64& t, uint16_t* dst, int tid) {
-  const int rq = tid & 15, ch = tid >> 4;
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&t.r[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&t.r[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&t.r[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&t.r[3]);
-  uint16_t* base = dst + (8 * ch) * TP + 4 * rq;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    *reinterpret_cast<uint2*>(base + (2 * e) * TP) = make_uint2(lo_pair(w0[e], w1[e]), lo_pair(w2[e], w3[e]));
-    *reinterpret_cast<uint2*>(base + (2 * e + 1) * TP) = make_uint2(hi_pair(w0[e], w1[e]), hi_pair(w2[e], w3[e]));
-  }
-}
-
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O): 16 lanes per row, rows of [B, L, Hq] in memory order.
-__global__ __launch_bounds__(kThreads) void bwd_dsum(BwdParams p) {
-  const int64_t gt = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+// 16 lanes per row, rows of [B, L, Hq] in memory order.
+__global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gt >> 4;
   const int ch = (int)(gt & 15);
   const int64_t nrows = (int64_t)p.B * p.L * p.Hq;
@@ -110,31 +73,32 @@ __global__ __launch_bounds__(kThreads) void bwd_dsum(BwdParams p) {
     const int h = (int)(row % p.Hq);
     const int64_t bi = row / p.Hq;
     const int i = (int)(bi % p.L), b = (int)(bi / p.L);
-    p.Dsum[((int64_t)b * p.Hq + h) * p.L + i] = s;
+    const int64_t o = ((int64_t)b * p.Hq + h) * p.L + i;
+    p.dl[o] = make_float2(s, p.lse[o] * kLog2e);
   }
 }
 
 // ---------------------------------------------------------------------------
-constexpr size_t kDkdvSmem = (2 * ROW_TILE + 2 * T_TILE) * sizeof(uint16_t) + 2 * 64 * sizeof(float);
+// dK / dV
+constexpr int kKvNW = 4;                       // waves per workgroup (32 keys each)
+constexpr int kKvNS = 3;                       // ring depth (query tiles)
+constexpr int kKvStage = 2 * kTileBytes + 512; // Q tile, dO tile, 64 x (D, LSE*log2e)
+constexpr size_t kDkdvSmem = (size_t)kKvNS * kKvStage;
 
-__global__ __launch_bounds__(kThreads) void bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Qs = smem;                     // [64][RP]   rows = queries
-  uint16_t* dOs = Qs + ROW_TILE;           // [64][RP]
-  uint16_t* Qt = dOs + ROW_TILE;           // [D][TP]    rows = head dim
-  uint16_t* dOt = Qt + T_TILE;             // [D][TP]
-  float* lse2_s = reinterpret_cast<float*>(dOt + T_TILE);  // [64] lse * log2(e)
-  float* D_s = lse2_s + 64;                                // [64]
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int L = p.L;
-  const int nkt = (L + 127) / 128;
+  const int nkt = (L + 32 * kKvNW - 1) / (32 * kKvNW);
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = wid % nkt;
   const int bk = wid / nkt;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-  const int k0 = kt * 128;
+  const int k0 = kt * 32 * kKvNW;
   const int kw0 = k0 + 32 * wave;          // this wave's first key
   const int key = kw0 + col;               // this lane's key (B-operand column)
   const int qmin_key = (min(key, L - 1) / p.blk) * p.blk;   // first query that sees `key`
@@ -142,55 +106,80 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv(BwdParams p) {
   const int qmin_w_hi = (min(kw0 + 31, L - 1) / p.blk) * p.blk;
   const int q_first = ((min(k0, L - 1) / p.blk) * p.blk / 64) * 64;
   const int nqt = (L - q_first + 63) / 64;
+  const int n_iter = p.G * nqt;
+  const bool wave_live = kw0 < L;
 
   const int64_t kv_rs = (int64_t)p.Hkv * D, q_rs = (int64_t)p.Hq * D;
+
+  // this wave's share of iteration `it`'s tiles: Q, dO rows and the (D, LSE) slice
+  auto issue = [&](int it) {
+    const uint32_t st = lds0 + (uint32_t)(it % kKvNS) * kKvStage;
+    const int hq = kvh * p.G + it / nqt;
+    const int q0 = q_first + (it % nqt) * 64;
+    const uint16_t* qb = p.q + (int64_t)b * L * q_rs + (int64_t)hq * D;
+    const uint16_t* dob = p.dO + (int64_t)b * L * q_rs + (int64_t)hq * D;
+    tile_dma<kKvNW>(st, qb, q_rs, q0, L, wave, lane);
+    tile_dma<kKvNW>(st + kTileBytes, dob, q_rs, q0, L, wave, lane);
+    // 64 float2 = 512 bytes: lanes 0..31 of every wave copy the same slice, rows
+    // q0 + 2l and q0 + 2l + 1 to slots 2l, 2l + 1.  When only the first row of a
+    // pair exists, the second read runs 8 bytes into the next head's rows (or
+    // into the workspace's 16 bytes of slack); lanes wholly past the end read
+    // from row 0.  Query rows past the end are masked below.
+    const float2* dlb = p.dl + ((int64_t)b * p.Hq + hq) * L;
+    const int r2 = q0 + 2 * lane;
+    if (lane < 32) lds_dma16(dlb + (r2 < L ? r2 : 0), st + 2 * kTileBytes);
+  };
+  for (int u = 0; u < kKvNS - 1 && u < n_iter; ++u) issue(u);
+
   bf16x8 kreg[8], vreg[8];
   {
-    const int64_t off = ((int64_t)b * L + key) * kv_rs + (int64_t)kvh * D + 8 * half;
+    const int64_t off = ((int64_t)b * L + min(key, L - 1)) * kv_rs + (int64_t)kvh * D + 8 * half;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       kreg[t] = as_bf16x8(key < L ? ldg16(p.k + off + 16 * t) : make_uint4(0, 0, 0, 0));
       vreg[t] = as_bf16x8(key < L ? ldg16(p.v + off + 16 * t) : make_uint4(0, 0, 0, 0));
     }
   }
+  vm_wait<0>();
+
   f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk_acc[db][i] = 0.f; dv_acc[db][i] = 0.f; }
 
-  const int arow = sigma32(col);
-  const int n_iter = p.G * nqt;
-  Tile64 tq, tdo;
-  float pre_lse = 0.f, pre_D = 0.f;
-  auto prefetch = [&](int it) {
-    const int hq = kvh * p.G + it / nqt;
-    const int q0 = q_first + (it % nqt) * 64;
-    const uint16_t* qb = p.q + (int64_t)b * L * q_rs + (int64_t)hq * D;
-    const uint16_t* db_ = p.dO + (int64_t)b * L * q_rs + (int64_t)hq * D;
-    tile_load(tq, [&](int r) { return qb + r * q_rs; }, q0, L, tid);
-    tile_load(tdo, [&](int r) { return db_ + r * q_rs; }, q0, L, tid);
-    if (tid < 64) {
-      const int qi = q0 + tid;
-      const int64_t s = ((int64_t)b * p.Hq + hq) * L + qi;
-      pre_lse = qi < L ? p.lse[s] * kLog2e : __builtin_huge_valf();
-      pre_D = qi < L ? p.Dsum[s] : 0.f;
-    }
-  };
+  // Per-lane LDS offsets within a stage: A-operand rows of Q / dO in sigma32
+  // order (logical chunk 2*ds + half), and the transposed-read addresses of Q^T /
+  // dO^T (as the forward's V^T reads).
+  uint32_t raddr[8], taddr[4][2];
+  {
+    const int rrow = sigma32(col);
+    const int rswz = tile_swz(rrow);
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) raddr[ds] = rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
+    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        taddr[db][x] = (8 * half + jj) * 256 + ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) + 8 * (li & 1);
+  }
+  const float c2 = p.scale_log2;
 
-  prefetch(0);
   for (int it = 0; it < n_iter; ++it) {
-    const int q0 = q_first + (it % nqt) * 64;
-    __syncthreads();   // previous tile fully consumed
-    tile_store_rows(tq, Qs, tid);
-    tile_store_rows(tdo, dOs, tid);
-    tile_store_transposed(tq, Qt, tid);
-    tile_store_transposed(tdo, dOt, tid);
-    if (tid < 64) { lse2_s[tid] = pre_lse; D_s[tid] = pre_D; }
+    {
+      const int pending = min(kKvNS - 2, n_iter - 1 - it);
+      constexpr int per = 2 * (16 / kKvNW) + 1;
+      if (pending >= 1) vm_wait<per>();
+      else vm_wait<0>();
+    }
     __syncthreads();
-    if (it + 1 < n_iter) prefetch(it + 1);
-
-    if (q0 + 64 <= qmin_w || kw0 >= L) continue;      // no query of the tile sees this wave's keys
+    if (it + kKvNS - 1 < n_iter) issue(it + kKvNS - 1);
+    const int q0 = q_first + (it % nqt) * 64;
+    if (!wave_live || q0 + 64 <= qmin_w) continue;      // no query of the tile sees this wave's keys
+    const uint32_t st = lds0 + (uint32_t)(it % kKvNS) * kKvStage;
+    const uint32_t Qt = st, dOt = st + kTileBytes;
+    const float2* dl_s = reinterpret_cast<const float2*>(reinterpret_cast<const char*>(smem) + (st - lds0) + 2 * kTileBytes);
     const bool partial = q0 < qmin_w_hi;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -198,43 +187,50 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv(BwdParams p) {
       f32x16 s_acc, dp_acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { s_acc[i] = 0.f; dp_acc[i] = 0.f; }
-      const uint16_t* qa = Qs + (32 * qs + arow) * RP + 8 * half;
-      const uint16_t* da = dOs + (32 * qs + arow) * RP + 8 * half;
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds) {
-        s_acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(qa + 16 * ds), kreg[ds], s_acc);
-        dp_acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(da + 16 * ds), vreg[ds], dp_acc);
+        s_acc = mfma_32x32x16(lds_read_b128(Qt + 32 * qs * 256 + raddr[ds]), kreg[ds], s_acc);
+        dp_acc = mfma_32x32x16(lds_read_b128(dOt + 32 * qs * 256 + raddr[ds]), vreg[ds], dp_acc);
       }
       // entry i of this lane holds query q0 + 32*qs + 16*(i/8) + 8*half + (i%8)
       float pv[16], dsv[16];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int qb0 = 32 * qs + 16 * j + 8 * half;
-        const float4 l0 = *reinterpret_cast<const float4*>(lse2_s + qb0);
-        const float4 l1 = *reinterpret_cast<const float4*>(lse2_s + qb0 + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(D_s + qb0);
-        const float4 d1 = *reinterpret_cast<const float4*>(D_s + qb0 + 4);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const float4* src = reinterpret_cast<const float4*>(dl_s + qb0);
+        float dd[8], ll[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 w = src[e];
+          dd[2 * e] = w.x; ll[2 * e] = w.y; dd[2 * e + 1] = w.z; ll[2 * e + 1] = w.w;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * j + e;
-          float pe = exp2_fast(s_acc[i] * p.scale_log2 - lv[e]);
+          float pe = exp2_fast(__builtin_fmaf(s_acc[i], c2, -ll[e]));
           if (partial && (q0 + qb0 + e) < qmin_key) pe = 0.f;
+          if (q0 + qb0 + e >= L) pe = 0.f;
           pv[i] = pe;
-          dsv[i] = pe * (dp_acc[i] - dv8[e]);
+          dsv[i] = pe * (dp_acc[i] - dd[e]);
         }
       }
       const bf16x8 pb0 = pack_bf16x8(pv), pb1 = pack_bf16x8(pv + 8);
       const bf16x8 sb0 = pack_bf16x8(dsv), sb1 = pack_bf16x8(dsv + 8);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* dta = dOt + (32 * db + col) * TP + 32 * qs + 8 * half;
-        const uint16_t* qta = Qt + (32 * db + col) * TP + 32 * qs + 8 * half;
-        dv_acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(dta), pb0, dv_acc[db]);
-        dv_acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(dta + 16), pb1, dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(qta), sb0, dk_acc[db]);
-        dk_acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(qta + 16), sb1, dk_acc[db]);
+        const int s0 = 2 * qs;   // 16-row k-steps 2qs, 2qs+1 of the 64-row tile
+        const bf16x8 dto0 = cat_i16x4(lds_read_tr16(dOt + taddr[db][s0 & 1] + (16 * s0) * 256),
+                                      lds_read_tr16(dOt + taddr[db][(s0 & 1) ^ 1] + (16 * s0 + 4) * 256));
+        const bf16x8 dto1 = cat_i16x4(lds_read_tr16(dOt + taddr[db][(s0 + 1) & 1] + (16 * (s0 + 1)) * 256),
+                                      lds_read_tr16(dOt + taddr[db][((s0 + 1) & 1) ^ 1] + (16 * (s0 + 1) + 4) * 256));
+        dv_acc[db] = mfma_32x32x16(dto0, pb0, dv_acc[db]);
+        dv_acc[db] = mfma_32x32x16(dto1, pb1, dv_acc[db]);
+        const bf16x8 qt0 = cat_i16x4(lds_read_tr16(Qt + taddr[db][s0 & 1] + (16 * s0) * 256),
+                                     lds_read_tr16(Qt + taddr[db][(s0 & 1) ^ 1] + (16 * s0 + 4) * 256));
+        const bf16x8 qt1 = cat_i16x4(lds_read_tr16(Qt + taddr[db][(s0 + 1) & 1] + (16 * (s0 + 1)) * 256),
+                                     lds_read_tr16(Qt + taddr[db][((s0 + 1) & 1) ^ 1] + (16 * (s0 + 1) + 4) * 256));
+        dk_acc[db] = mfma_32x32x16(qt0, sb0, dk_acc[db]);
+        dk_acc[db] = mfma_32x32x16(qt1, sb1, dk_acc[db]);
       }
     }
   }
@@ -257,25 +253,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-constexpr size_t kDqSmem = 2 * (2 * ROW_TILE + T_TILE) * sizeof(uint16_t);
+// dQ
+constexpr int kDqNW = 8;
+constexpr int kDqStage = 2 * kTileBytes;       // K tile, V tile
+constexpr size_t kDqSmem = 2 * (size_t)kDqStage;
 
-__global__ __launch_bounds__(kThreads) void bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // per buffer: K rows [64][RP], V rows [64][RP], K^T [D][TP]
-  constexpr int BUF = 2 * ROW_TILE + T_TILE;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int L = p.L;
-  const int qtiles = (L + 127) / 128;
+  const int qtiles = (L + 32 * kDqNW - 1) / (32 * kDqNW);
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = qtiles * p.G;
   const int grp = wid / per_group, rem = wid - grp * per_group;
   const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
   const int qt = qtiles - 1 - rem / p.G;
   const int hq = kvh * p.G + rem % p.G;
-  const int wg_r0 = qt * 128, r0 = wg_r0 + 32 * wave;
-  const int kend_wg = key_limit(min(wg_r0 + 128, L) - 1, L, p.blk);
+  const int wg_r0 = qt * 32 * kDqNW, r0 = wg_r0 + 32 * wave;
+  const int kend_wg = key_limit(min(wg_r0 + 32 * kDqNW, L) - 1, L, p.blk);
   const int ntiles = (kend_wg + 63) / 64;
   const bool active = r0 < L;
   const int kend_lo = active ? key_limit(r0, L, p.blk) : 0;
@@ -286,18 +285,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dq(BwdParams p) {
   const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
+  auto issue = [&](int t) {
+    const uint32_t st = lds0 + (uint32_t)(t & 1) * kDqStage;
+    tile_dma<kDqNW>(st, kb, kv_rs, t * 64, kend_wg, wave, lane);
+    tile_dma<kDqNW>(st + kTileBytes, vb, kv_rs, t * 64, kend_wg, wave, lane);
+  };
+  if (ntiles > 0) issue(0);
+
   bf16x8 qreg[8], doreg[8];
   {
-    const int64_t off = ((int64_t)b * L + qrow) * q_rs + (int64_t)hq * D + 8 * half;
+    const int64_t off = ((int64_t)b * L + min(qrow, L - 1)) * q_rs + (int64_t)hq * D + 8 * half;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       qreg[t] = as_bf16x8(qrow < L ? ldg16(p.q + off + 16 * t) : make_uint4(0, 0, 0, 0));
       doreg[t] = as_bf16x8(qrow < L ? ldg16(p.dO + off + 16 * t) : make_uint4(0, 0, 0, 0));
     }
   }
-  const int64_t srow = ((int64_t)b * p.Hq + hq) * L + min(qrow, L - 1);
-  const float lse2 = p.lse[srow] * kLog2e;
-  const float Dq = p.Dsum[srow];
+  const float2 dl = p.dl[((int64_t)b * p.Hq + hq) * L + min(qrow, L - 1)];
+  const float Dq = dl.x, nlse2 = -dl.y;
+  vm_wait<0>();
 
   f32x16 acc[4];
 #pragma unroll
@@ -305,72 +311,68 @@ __global__ __launch_bounds__(kThreads) void bwd_dq(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  Tile64 tk, tv;
-  auto kptr = [&](int r) { return kb + r * kv_rs; };
-  auto vptr = [&](int r) { return vb + r * kv_rs; };
-  tile_load(tk, kptr, 0, kend_wg, tid);
-  tile_load(tv, vptr, 0, kend_wg, tid);
-  tile_store_rows(tk, smem, tid);
-  tile_store_rows(tv, smem + ROW_TILE, tid);
-  tile_store_transposed(tk, smem + 2 * ROW_TILE, tid);
-  __syncthreads();
-  const int arow = sigma32(col);
+  uint32_t raddr[8], taddr[4][2];
+  {
+    const int rrow = sigma32(col);
+    const int rswz = tile_swz(rrow);
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) raddr[ds] = lds0 + rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
+    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        taddr[db][x] = lds0 + (8 * half + jj) * 256 + ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) +
+                       8 * (li & 1);
+  }
+  const float c2 = p.scale_log2;
 
-  for (int t = 0; t < ntiles; ++t) {
-    uint16_t* cur = smem + (t & 1) * BUF;
-    if (t + 1 < ntiles) {
-      tile_load(tk, kptr, (t + 1) * 64, kend_wg, tid);
-      tile_load(tv, vptr, (t + 1) * 64, kend_wg, tid);
-    }
+  auto step = [&](auto stage_c, int t) {
+    constexpr uint32_t so = decltype(stage_c)::value * kDqStage;
+    vm_wait<0>();
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1);
     const int key0 = t * 64;
-    if (active && key0 < kend_hi) {
-      const uint16_t* Ks = cur;
-      const uint16_t* Vs = cur + ROW_TILE;
-      const uint16_t* Kt = cur + 2 * ROW_TILE;
-      f32x16 s_acc[2], dp_acc[2];
+    if (!active || key0 >= kend_hi) return;
+    const bool partial = key0 + 64 > kend_lo;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x16 s_acc, dp_acc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s_acc[h2][i] = 0.f; dp_acc[h2][i] = 0.f; }
-        const uint16_t* ka = Ks + (32 * h2 + arow) * RP + 8 * half;
-        const uint16_t* va = Vs + (32 * h2 + arow) * RP + 8 * half;
+      for (int i = 0; i < 16; ++i) { s_acc[i] = 0.f; dp_acc[i] = 0.f; }
 #pragma unroll
-        for (int ds = 0; ds < 8; ++ds) {
-          s_acc[h2] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ka + 16 * ds), qreg[ds], s_acc[h2]);
-          dp_acc[h2] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(va + 16 * ds), doreg[ds], dp_acc[h2]);
-        }
+      for (int ds = 0; ds < 8; ++ds) {
+        s_acc = mfma_32x32x16(lds_read_b128(raddr[ds] + so + h2 * 32 * 256), qreg[ds], s_acc);
+        dp_acc = mfma_32x32x16(lds_read_b128(raddr[ds] + so + kTileBytes + h2 * 32 * 256), doreg[ds], dp_acc);
       }
-      const bool partial = key0 + 64 > kend_lo;
-      bf16x8 sb[4];
+      // entry i holds key key0 + 32*h2 + 16*(i/8) + 8*half + (i%8)
+      bf16x8 sb[2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int j = 0; j < 2; ++j) {
+        float dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * j + e;
+          float pe = exp2_fast(__builtin_fmaf(s_acc[i], c2, nlse2));
+          if (partial && key0 + 32 * h2 + 16 * j + 8 * half + e >= kq) pe = 0.f;
+          dsv[e] = pe * (dp_acc[i] - Dq);
+        }
+        sb[j] = pack_bf16x8(dsv);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          float dsv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * j + e;
-            float pe = exp2_fast(s_acc[h2][i] * p.scale_log2 - lse2);
-            if (partial && key0 + 32 * h2 + 16 * j + 8 * half + e >= kq) pe = 0.f;
-            dsv[e] = pe * (dp_acc[h2][i] - Dq);
-          }
-          sb[2 * h2 + j] = pack_bf16x8(dsv);
+          const int s4 = 2 * h2 + j;
+          const i16x4 lo = lds_read_tr16(taddr[db][s4 & 1] + so + (16 * s4) * 256);
+          const i16x4 hi = lds_read_tr16(taddr[db][(s4 & 1) ^ 1] + so + (16 * s4 + 4) * 256);
+          acc[db] = mfma_32x32x16(cat_i16x4(lo, hi), sb[j], acc[db]);
         }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* ka = Kt + (32 * db + col) * TP + 8 * half;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          acc[db] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ka + 16 * s4), sb[s4], acc[db]);
-      }
     }
-    if (t + 1 < ntiles) {
-      uint16_t* nxt = smem + ((t + 1) & 1) * BUF;
-      tile_store_rows(tk, nxt, tid);
-      tile_store_rows(tv, nxt + ROW_TILE, tid);
-      tile_store_transposed(tk, nxt + 2 * ROW_TILE, tid);
-    }
-    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>(), t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
   }
 
   if (!active || qrow >= L) return;
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq(BwdParams p) {
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int batch, int seqlen, int n_q_heads) {
-  return (size_t)batch * n_q_heads * seqlen * sizeof(float);
+  return (size_t)batch * n_q_heads * seqlen * sizeof(float2) + 16;
 }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -412,7 +414,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.o = static_cast<const uint16_t*>(o);
   p.dO = static_cast<const uint16_t*>(d_o);
   p.lse = lse;
-  p.Dsum = static_cast<float*>(ws);
+  p.dl = static_cast<float2*>(ws);
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
@@ -425,15 +427,15 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.scale = s.scale;
   p.scale_log2 = s.scale * kLog2e;
   const long long rows = (long long)s.batch * s.seqlen * s.n_q_heads;
-  hipLaunchKernelGGL(bwd_dsum, dim3((unsigned)((rows * 16 + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + 127) / 128);
-  hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)nk), dim3(kThreads), kDkdvSmem, st, p);
+  const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + 32 * kKvNW - 1) / (32 * kKvNW));
+  hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)nk), dim3(kKvNW * 64), kDkdvSmem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nq = (long long)s.batch * s.n_q_heads * ((s.seqlen + 127) / 128);
-  hipLaunchKernelGGL(bwd_dq, dim3((unsigned)nq), dim3(kThreads), kDqSmem, st, p);
+  const long long nq = (long long)s.batch * s.n_q_heads * ((s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW));
+  hipLaunchKernelGGL(bwd_dq, dim3((unsigned)nq), dim3(kDqNW * 64), kDqSmem, st, p);
   return hipGetLastError();
 }
 

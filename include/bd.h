@@ -95,8 +95,9 @@ bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   dq  [batch, seqlen, n_q_heads, head_dim]       out
  *   dk, dv [batch, seqlen, n_kv_heads, head_dim]   out (summed over the query
  *        heads of each group)
- *   workspace of bd_attn_bwd_workspace_size() bytes (holds the per-row
- *        D = rowsum(d_o * o) in float32); contents on entry are ignored.
+ *   workspace of bd_attn_bwd_workspace_size() bytes (holds, per row, D =
+ *        rowsum(d_o * o) and lse * log2(e) in float32); contents on entry are
+ *        ignored.
  *
  * Supported: as bd_attn_fwd.  Deterministic: no atomics.
  * ---------------------------------------------------------------------- */
