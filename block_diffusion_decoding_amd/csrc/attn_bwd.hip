@@ -151,18 +151,13 @@ __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
   // Per-lane LDS offsets within a stage: A-operand rows of Q / dO in sigma32
   // order (logical chunk 2*ds + half), and the transposed-read addresses of Q^T /
   // dO^T (as the forward's V^T reads).
-  uint32_t raddr[8], taddr[4][2];
+  uint32_t raddr[8], taddr[8];
   {
     const int rrow = sigma32(col);
     const int rswz = tile_swz(rrow);
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) raddr[ds] = rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
-    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        taddr[db][x] = (8 * half + jj) * 256 + ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) + 8 * (li & 1);
+    tr32_bases(taddr, 0, lane);
   }
   const float c2 = p.scale_log2;
 
@@ -219,16 +214,16 @@ __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int s0 = 2 * qs;   // 16-row k-steps 2qs, 2qs+1 of the 64-row tile
-        const bf16x8 dto0 = cat_i16x4(lds_read_tr16(dOt + taddr[db][s0 & 1] + (16 * s0) * 256),
-                                      lds_read_tr16(dOt + taddr[db][(s0 & 1) ^ 1] + (16 * s0 + 4) * 256));
-        const bf16x8 dto1 = cat_i16x4(lds_read_tr16(dOt + taddr[db][(s0 + 1) & 1] + (16 * (s0 + 1)) * 256),
-                                      lds_read_tr16(dOt + taddr[db][((s0 + 1) & 1) ^ 1] + (16 * (s0 + 1) + 4) * 256));
+        const bf16x8 dto0 = cat_i16x4(lds_read_tr16(dOt + taddr[tr32_idx(db, s0, 0)] + tr32_off(s0, 0)),
+                                      lds_read_tr16(dOt + taddr[tr32_idx(db, s0, 1)] + tr32_off(s0, 1)));
+        const bf16x8 dto1 = cat_i16x4(lds_read_tr16(dOt + taddr[tr32_idx(db, s0 + 1, 0)] + tr32_off(s0 + 1, 0)),
+                                      lds_read_tr16(dOt + taddr[tr32_idx(db, s0 + 1, 1)] + tr32_off(s0 + 1, 1)));
         dv_acc[db] = mfma_32x32x16(dto0, pb0, dv_acc[db]);
         dv_acc[db] = mfma_32x32x16(dto1, pb1, dv_acc[db]);
-        const bf16x8 qt0 = cat_i16x4(lds_read_tr16(Qt + taddr[db][s0 & 1] + (16 * s0) * 256),
-                                     lds_read_tr16(Qt + taddr[db][(s0 & 1) ^ 1] + (16 * s0 + 4) * 256));
-        const bf16x8 qt1 = cat_i16x4(lds_read_tr16(Qt + taddr[db][(s0 + 1) & 1] + (16 * (s0 + 1)) * 256),
-                                     lds_read_tr16(Qt + taddr[db][((s0 + 1) & 1) ^ 1] + (16 * (s0 + 1) + 4) * 256));
+        const bf16x8 qt0 = cat_i16x4(lds_read_tr16(Qt + taddr[tr32_idx(db, s0, 0)] + tr32_off(s0, 0)),
+                                     lds_read_tr16(Qt + taddr[tr32_idx(db, s0, 1)] + tr32_off(s0, 1)));
+        const bf16x8 qt1 = cat_i16x4(lds_read_tr16(Qt + taddr[tr32_idx(db, s0 + 1, 0)] + tr32_off(s0 + 1, 0)),
+                                     lds_read_tr16(Qt + taddr[tr32_idx(db, s0 + 1, 1)] + tr32_off(s0 + 1, 1)));
         dk_acc[db] = mfma_32x32x16(qt0, sb0, dk_acc[db]);
         dk_acc[db] = mfma_32x32x16(qt1, sb1, dk_acc[db]);
       }
@@ -311,19 +306,13 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  uint32_t raddr[8], taddr[4][2];
+  uint32_t raddr[8], taddr[8];
   {
     const int rrow = sigma32(col);
     const int rswz = tile_swz(rrow);
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) raddr[ds] = lds0 + rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
-    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        taddr[db][x] = lds0 + (8 * half + jj) * 256 + ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) +
-                       8 * (li & 1);
+    tr32_bases(taddr, lds0, lane);
   }
   const float c2 = p.scale_log2;
 
@@ -364,8 +353,8 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int s4 = 2 * h2 + j;
-          const i16x4 lo = lds_read_tr16(taddr[db][s4 & 1] + so + (16 * s4) * 256);
-          const i16x4 hi = lds_read_tr16(taddr[db][(s4 & 1) ^ 1] + so + (16 * s4 + 4) * 256);
+          const i16x4 lo = lds_read_tr16(taddr[tr32_idx(db, s4, 0)] + so + tr32_off(s4, 0));
+          const i16x4 hi = lds_read_tr16(taddr[tr32_idx(db, s4, 1)] + so + tr32_off(s4, 1));
           acc[db] = mfma_32x32x16(cat_i16x4(lo, hi), sb[j], acc[db]);
         }
     }

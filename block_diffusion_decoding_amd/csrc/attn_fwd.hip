@@ -46,19 +46,15 @@ namespace {
 
 constexpr int D = 128;
 constexpr int KT = 64;                    // keys per tile
-#ifndef BD_FWD_NW
-#define BD_FWD_NW 8
-#endif
-#ifndef BD_FWD_NS
-#define BD_FWD_NS 2
-#endif
-constexpr int kNW = BD_FWD_NW;            // waves per workgroup
-constexpr int kNS = BD_FWD_NS;            // LDS ring depth (tiles)
+constexpr int kNW = 8;                    // waves per workgroup (two per SIMD)
 constexpr int kThreads = kNW * 64;
 constexpr int kTileBytes = KT * D * 2;    // 16 KB
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr size_t kSmemBytes = (size_t)kNS * kStageBytes;
-constexpr float kRescaleSlack = 8.0f;     // log2 units
+constexpr int kNS = 3;                    // ring depth (K and V each)
+constexpr uint32_t kKRing = 0;
+constexpr uint32_t kVRing = kNS * kTileBytes;
+constexpr uint32_t kIdsOff = 2 * kNS * kTileBytes;   // per-wave SIMD ids
+constexpr size_t kSmemBytes = 2 * kNS * kTileBytes + 64;
+constexpr float kSumLimit = 65536.0f;     // 2^16: largest accepted per-lane tile sum
 
 struct FwdParams {
   const uint16_t* q;
@@ -102,11 +98,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
 
-  static_assert(kNS == 2, "the tile loop below is written for a two-stage ring");
-  // prologue: tile 0 in flight
-  if (ntiles > 0) {
-    tile_dma<kNW>(lds0, kb, kv_rs, 0, kend_wg, wave, lane);
-    tile_dma<kNW>(lds0 + kTileBytes, vb, kv_rs, 0, kend_wg, wave, lane);
+  // SIMD of this wave (HW_ID bits 5:4); exchanged through LDS below.
+  const int simd = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* simd_of = reinterpret_cast<lds_int*>((uintptr_t)(lds0 + kIdsOff));
+  if (lane == 0) simd_of[wave] = simd;
+
+  // Prologue: K tiles 0 and 1 and V tile 0 (issued by all waves), and the V
+  // stage of tile -1 zero-filled (the first matrix phase multiplies it by
+  // P = 0).
+  for (int u = 0; u < 2 && u < ntiles; ++u)
+    tile_dma<kNW>(lds0 + kKRing + u * kTileBytes, kb, kv_rs, u * KT, kend_wg, wave, lane);
+  if (ntiles > 0) tile_dma<kNW>(lds0 + kVRing, vb, kv_rs, 0, kend_wg, wave, lane);
+  {
+    uint4* vz = reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + kVRing + (kNS - 1) * kTileBytes);
+    vz[tid] = make_uint4(0, 0, 0, 0);
+    vz[tid + kThreads] = make_uint4(0, 0, 0, 0);
   }
 
   bf16x8 qreg[8];
@@ -116,6 +123,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
     if (qrow < L) u = ldg16(qb + qrow * q_rs + 16 * t + 8 * half);
     qreg[t] = as_bf16x8(u);
   }
+  vm_wait<0>();
+  __syncthreads();
+
+  // Wave groups.  Normally the hardware places two waves on each SIMD: group A
+  // is the first of the two (by wave index), group B the second, and gw (0..3)
+  // is the SIMD.  Otherwise waves 0-3 form A and 4-7 form B, gw = wave % 4.
+  // Either way each group has four waves with distinct gw (which split the
+  // group's tile loads); the pairing only affects speed.
+  int ids[kNW];
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) ids[w] = __builtin_amdgcn_readfirstlane(simd_of[w]);
+  bool paired = true;
+  int rank = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    int same = 0;
+#pragma unroll
+    for (int x = 0; x < kNW; ++x) same += (ids[x] == ids[w]);
+    paired = paired && same == 2;
+    rank += (w < wave && ids[w] == simd);
+  }
+  const bool grp_a = __builtin_amdgcn_readfirstlane(paired ? rank == 0 : wave < 4);
+  const int gw = __builtin_amdgcn_readfirstlane(paired ? simd : (wave & 3));
 
   f32x16 oacc[4];
 #pragma unroll
@@ -125,53 +155,104 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   float m_use = kNegInf, l_run = 0.f;
   const float c2 = p.scale_log2;
 
-  // Per-lane LDS byte addresses (stage 0), so that every read below is this
-  // register plus a compile-time offset.
+  // Per-lane LDS byte addresses, so that every read below is one of these
+  // registers plus a compile-time offset.
   //   K A operand, d-step ds: row sigma32(col) (+32 for the second key block),
-  //     logical chunk 2*ds + half.
-  //   V^T A operand (transposed read), d-block db, k-step s4, half-read tt:
-  //     row 16*s4 + 8*half + 4*tt + jj, logical chunk 4*db + 2*g1 + b, where
-  //     jj = (lane%16)/4, g1 = (lane/16)%2, b = (lane%4)/2; with tile_swz the
-  //     physical chunk is 4*(db^jj) + 2*(g1^half) + (b ^ tt ^ (s4%2)).
-  uint32_t kaddr[8], vaddr[4][2];
+  //     logical chunk 2*ds + half (K stage of the current tile).
+  //   V^T A operand: the transposed-read table of bd_device.hpp (V stage of the
+  //     previous tile).
+  uint32_t kaddr[8], vaddr[8];
   {
     const int krow = sigma32(col);
     const int kswz = tile_swz(krow);
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) kaddr[ds] = lds0 + krow * 256 + (((2 * ds + half) ^ kswz) << 4);
-    const int li = lane & 15, jj = li >> 2, g1 = (lane >> 4) & 1, bb = (li & 3) >> 1;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        vaddr[db][x] = lds0 + kTileBytes + (8 * half + jj) * 256 +
-                       ((4 * (db ^ jj) + 2 * (g1 ^ half) + (bb ^ x)) << 4) + 8 * (li & 1);
+    for (int ds = 0; ds < 8; ++ds) kaddr[ds] = lds0 + kKRing + krow * 256 + (((2 * ds + half) ^ kswz) << 4);
+    tr32_bases(vaddr, lds0 + kVRing + (kNS - 1) * kTileBytes, lane);
   }
 
-  auto step = [&](auto stage_c, int t) {
-    constexpr int S = decltype(stage_c)::value;
-    constexpr uint32_t so = S * kStageBytes;
-    vm_wait<0>();
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      const uint32_t st = lds0 + (1 - S) * kStageBytes;
-      tile_dma<kNW>(st, kb, kv_rs, (t + 1) * KT, kend_wg, wave, lane);
-      tile_dma<kNW>(st + kTileBytes, vb, kv_rs, (t + 1) * KT, kend_wg, wave, lane);
-    }
-    const int key0 = t * KT;
-    if (!active || key0 >= kend_hi) return;
+  auto live = [&](int t) __attribute__((always_inline)) { return active && t * KT < kend_hi; };
 
-    f32x16 sacc[2];
+  // Group loads: a group's four waves split one tile (4 x 1 KB each).  All
+  // tiles but the workgroup's last have 64 existing rows and use fixed per-lane
+  // offsets from a uniform base; the last one clamps its rows to kend_wg - 1.
+  uint32_t dma_off[4];
+  tile_dma_offsets<4>(dma_off, kv_rs, gw, lane);
+  auto load_tile = [&](uint32_t lds_tile, const uint16_t* g, int u) __attribute__((always_inline)) {
+    if (u + 1 < ntiles) tile_dma_full<4>(lds_tile, g + (int64_t)u * KT * kv_rs, dma_off, gw);
+    else tile_dma<4>(lds_tile, g, kv_rs, u * KT, kend_wg, gw, lane);
+  };
+  f32x16 sacc[2];
+  bf16x8 pb[4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+  for (int j = 0; j < 4; ++j) pb[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+
+  // The products of a matrix phase, interleaved: PV product i (d-block i%4,
+  // k-step i/4) and QK product i (key block i%2, d-step i/2) alternate, so
+  // products into the same accumulator are 4 to 8 apart, and the operands of
+  // the next kLook steps are read from LDS while a step is multiplied.
+  auto mm = [&]() __attribute__((always_inline)) {
+    constexpr int kLook = 4;
+    bf16x8 vop[16], kop[16];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[h2][i] = 0.f;
+    auto read_step = [&](int i) __attribute__((always_inline)) {
+      const int db = i & 3, s4 = i >> 2;
+      vop[i] = cat_i16x4(lds_read_tr16(vaddr[tr32_idx(db, s4, 0)] + tr32_off(s4, 0)),
+                         lds_read_tr16(vaddr[tr32_idx(db, s4, 1)] + tr32_off(s4, 1)));
+      kop[i] = lds_read_b128(kaddr[i >> 1] + (i & 1) * 32 * 256);
+    };
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds)
-        sacc[h2] = mfma_32x32x16(lds_read_b128(kaddr[ds] + so + h2 * 32 * 256), qreg[ds], sacc[h2]);
+    for (int i = 0; i < kLook; ++i) read_step(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kLook, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + kLook < 16) read_step(i + kLook);
+      oacc[i & 3] = mfma_32x32x16(vop[i], pb[i >> 2], oacc[i & 3]);
+      sacc[i & 1] = mfma_32x32x16(kop[i], qreg[i >> 1], sacc[i & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i + kLook < 16) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
+  };
+
+  // P = exp2(S * scale * log2 e - m_use) packed to bf16, and this lane's share
+  // of the row sums.  Per block of 8 scores: 8 FMAs, 8 exponentials, then the
+  // sums (two partial sums) and packs, so that no exponential waits on the FMA
+  // just before it.
+  auto exp_tile = [&](float nm) __attribute__((always_inline)) {
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float x8[8], pv8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x8[e] = __builtin_fmaf(sacc[h2][8 * j + e], c2, nm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv8[e] = exp2_fast(x8[e]);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          ps0 += pv8[e];
+          ps1 += pv8[e + 1];
+        }
+        pb[2 * h2 + j] = pack_bf16x8(pv8);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);   // FMAs
+        __builtin_amdgcn_sched_group_barrier(0x400, 8, 1);   // exponentials
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 1);  // sums, packs
+      }
+    return ps0 + ps1;
+  };
+
+  // Softmax of one tile.  The exponent offset m_use is not the running maximum:
+  // it is raised only when the tile's exponentials with the current offset
+  // would exceed 2^16 (or on a column's first visible tile, where it is -inf),
+  // so the common case needs no maximum at all.  Either way O and the row sum
+  // share the offset, so the result is exact up to rounding; values stay below
+  // 2^16 times the row sum of an ordinary softmax.
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * KT;
     // entry i of block h2 holds key key0 + 32*h2 + 16*(i/8) + 8*half + (i%8)
-    float mx = kNegInf;
     if (key0 + KT > kend_lo) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -179,59 +260,91 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * h2 + 16 * (i >> 3) + 8 * half + (i & 7);
           if (key >= kq) sacc[h2][i] = kNegInf;
-          mx = fmaxf(mx, sacc[h2][i]);
         }
-    } else {
+    }
+    float psum = exp_tile(-m_use);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSumLimit))) {
+      float mx = kNegInf;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[h2][i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    const bool grow = mx > m_use + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_use;
-      const float alpha = exp2_fast(m_use - m_new);
-      m_use = m_new;
-      l_run *= alpha;
+      mx = pair_max(mx) * c2;   // column maximum (both halves of the column)
+      if (mx > m_use) {
+        const float alpha = exp2_fast(m_use - mx);   // 0 while m_use is -inf
+        m_use = mx;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-    const float nm = -m_use;
-    float psum = 0.f;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2_fast(__builtin_fmaf(sacc[h2][8 * j + e], c2, nm));
-          psum += pv[e];
-        }
-        pb[2 * h2 + j] = pack_bf16x8(pv);
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
+      // a column with no visible key so far keeps m_use = -inf and p = 0
+      psum = exp_tile(m_use == kNegInf ? 0.f : -m_use);
+    }
     l_run += psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const i16x4 lo = lds_read_tr16(vaddr[db][s4 & 1] + so + (16 * s4) * 256);
-        const i16x4 hi = lds_read_tr16(vaddr[db][(s4 & 1) ^ 1] + so + (16 * s4 + 4) * 256);
-        oacc[db] = mfma_32x32x16(cat_i16x4(lo, hi), pb[s4], oacc[db]);
-      }
   };
 
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>(), t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
+  // The softmax phase: its group's load of tile u into lds_tile (if any, waited
+  // for two phases later) and the softmax of tile ts (if this wave's rows see
+  // it).
+  auto s_phase = [&](uint32_t lds_tile, const uint16_t* g, int u, int ts) __attribute__((always_inline)) {
+    const bool ld = u < ntiles;
+    if (ld) load_tile(lds_tile, g, u);
+    if (ts >= 0 && ts < ntiles && live(ts)) softmax(ts);
+    if (ld) vm_wait<4>();
+    else vm_wait<0>();
+  };
+
+  // The matrix phase of tile t: O += P(t-1) V(t-1) and S(t) = Q K(t)^T.  One
+  // code path for every phase keeps the live ranges short: for t = 0 the PV
+  // products multiply P = 0 by the zero-filled V stage, and when tile t is past
+  // this wave's rows (or past the last tile) the QK products run on whatever
+  // the K stage holds and their result is never used.  Afterwards kaddr moves
+  // to the K stage of tile t+1 and vaddr to the V stage of tile t.
+  int kst = 0, vst = kNS - 1;   // ring stages of K(t) and V(t-1)
+  auto m_phase = [&](int t) __attribute__((always_inline)) {
+    if (live(t == 0 ? 0 : t - 1)) mm();
+    const uint32_t dk = kst == kNS - 1 ? (uint32_t)(-(kNS - 1) * kTileBytes) : (uint32_t)kTileBytes;
+    const uint32_t dv = vst == kNS - 1 ? (uint32_t)(-(kNS - 1) * kTileBytes) : (uint32_t)kTileBytes;
+    kst = kst == kNS - 1 ? 0 : kst + 1;
+    vst = vst == kNS - 1 ? 0 : vst + 1;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) kaddr[ds] += dk;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) vaddr[y] += dv;
+  };
+
+  // Schedule.  Every tile takes two phases, each ended by a workgroup
+  // barrier.  Group A runs, in phase 2t, the products O += P(t-1) V(t-1) and
+  // S(t) = Q K(t)^T, and in phase 2t+1 the softmax of S(t); group B runs the
+  // same one phase later.  So in every phase one wave of each SIMD issues
+  // matrix products while the other runs its softmax on the vector ALU.
+  // Loads are issued only in softmax phases, so that the matrix phases never
+  // wait on the memory pipeline: A starts K(t+2) in phase 2t+1, B starts V(t+1)
+  // in phase 2t, and each waits for its previous load at the end of that
+  // phase, two phases after issuing it (K(t+1) is first read in phase 2t+2,
+  // V(t) in phase 2t+2).  With three stages per ring, a load never overwrites
+  // a tile still to be read: K(t-1) and V(t-2), whose stages K(t+2) and V(t+1)
+  // take, were last read in phase 2t-1.
+  if (grp_a) {
+    for (int t = 0; t <= ntiles; ++t) {
+      m_phase(t);
+      __syncthreads();
+      s_phase(lds0 + kKRing + ((t + 2) % kNS) * kTileBytes, kb, t + 2, t);
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t <= ntiles; ++t) {
+      s_phase(lds0 + kVRing + ((t + 1) % kNS) * kTileBytes, vb, t + 1, t - 1);
+      __syncthreads();
+      m_phase(t);
+      __syncthreads();
+    }
   }
 
   if (!active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   if (qrow >= L) return;
   const float inv = 1.0f / l_tot;
   uint16_t* orow = p.o + ((int64_t)b * L + qrow) * q_rs + (int64_t)hq * D;
