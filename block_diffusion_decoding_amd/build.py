@@ -27,11 +27,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wno-unused-command-line-argument"]
 
 SOURCES = ["bd_api.cpp", "commit.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip"]
+# The decode kernel keeps its matrix accumulators in ordinary VGPRs (otherwise
+# the compiler parks them in AGPRs and copies them back and forth every tile).
+PER_FILE = {"attn_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, verbose: bool, build_dir: str, defines: dict) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *[f"-D{k}={v}" for k, v in defines.items()], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *[f"-D{k}={v}" for k, v in defines.items()], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,8 +51,8 @@ def build(verbose: bool = False, defines: dict | None = None, lib_path: str | No
           build_dir: str | None = None) -> str:
     """Compile all sources and link the library; returns its path.
 
-    ``defines`` overrides the compile-time pipeline shapes (BD_FWD_NW, BD_FWD_NS,
-    BD_DECODE_NS, BD_DECODE_TARGET_WGS); with ``lib_path`` the result is written
+    ``defines`` overrides the compile-time pipeline shapes (BD_DECODE_NS,
+    BD_DECODE_TARGET_WGS); with ``lib_path`` the result is written
     elsewhere instead of replacing the package's libbd.so.
     """
     defines = dict(defines or {})

@@ -3,21 +3,29 @@
 // mask (the block is the newest one; paper.rainbus.top digest, novelty
 // paragraph on KV-cache reuse across blocks).
 //
-// Split-KV ("flash decoding") on gfx950:
-//   decode_split  one workgroup per (sequence, kv head, row tile of 64 query
-//                 rows = block tokens x the query heads of the group, key
-//                 split).  Four waves own 16 query rows each and share K/V
-//                 tiles of 32 keys copied global -> LDS directly into a ring of
-//                 kNS swizzled stages (kNS-1 tiles of loads in flight; 48 KB of
-//                 LDS, so three workgroups share a CU).  Per tile and wave:
+// Balanced split-KV on gfx950.  Per KV head and row tile (64 query rows = block
+// tokens x the query heads of the group) the key tiles of all sequences form
+// one line: sequence 0's tiles of 32 keys (prefix keys, then the block's own),
+// then sequence 1's, and so on.  The line is cut into R equal contiguous
+// ranges, one workgroup each, with R chosen so that about one workgroup per
+// resident slot of the chip is launched: every workgroup streams the same
+// number of tiles whatever the mix of prefix lengths.
+//   decode_split  workgroup = (range, row tile, kv head), kv head fastest so
+//                 that neighbouring workgroups read neighbouring pieces of the
+//                 same cache rows.  Four waves own 16 query rows each and share
+//                 K/V tiles copied global -> LDS directly into a ring of kNS
+//                 swizzled stages that runs on across sequence boundaries.  Per
+//                 tile and wave:
 //                   S^T[32 keys x 16 q] = K Q^T  (2 x 4 MFMA 16x16x32)
 //                   O^T[128 d x 16 q]  += V^T P^T (8 MFMA 16x16x32, V^T read
 //                                                  transposed from LDS)
-//                 and writes its unnormalised partial (m, l, acc) in fp32.
-//   decode_merge  combines the splits exactly: m = max m_s,
-//                 l = sum l_s 2^(m_s - m), O = sum acc_s 2^(m_s - m) / l, and
-//                 writes O (bf16) and LSE; 128 threads per query row, one per
-//                 head-dim entry.
+//                 At the end of each sequence's segment of the range it writes
+//                 the unnormalised partial state (m, l, acc) in fp32 to slot
+//                 range + sequence (distinct for every pair a range meets).
+//   decode_merge  combines the partials of each sequence exactly:
+//                 m = max m_s, l = sum l_s 2^(m_s - m),
+//                 O = sum acc_s 2^(m_s - m) / l, and writes O (bf16) and LSE;
+//                 32 threads per query row, four head-dim entries each.
 // Each K/V byte of the cache is read from HBM once per step.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
@@ -25,13 +33,13 @@
 #include <algorithm>
 #include <mutex>
 
-// Pipeline shape (compile-time): LDS ring depth and the workgroup count the
-// split plan aims for.
+// Pipeline shape (compile-time): LDS ring depth, and the number of workgroups
+// the plan aims for (256 compute units x 3 resident workgroups of 48 KB LDS).
 #ifndef BD_DECODE_NS
 #define BD_DECODE_NS 3
 #endif
 #ifndef BD_DECODE_TARGET_WGS
-#define BD_DECODE_TARGET_WGS 4096
+#define BD_DECODE_TARGET_WGS 768
 #endif
 
 namespace bd {
@@ -46,7 +54,8 @@ constexpr int kRows = 64;                     // query rows per workgroup (4 wav
 constexpr int kTileBytes = KT * D * 2;      // 8 KB
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr size_t kSmemBytes = (size_t)kNS * kStageBytes;
-constexpr int kMergeRows = 2;                 // query rows per merge workgroup
+constexpr int kMergeRows = 8;                 // query rows per merge workgroup
+constexpr int kMinRangeTiles = 2;             // fewest tiles per range the plan aims for
 
 struct DecParams {
   const uint16_t* q_blk;
@@ -56,17 +65,87 @@ struct DecParams {
   const uint16_t* v_cache;
   const int64_t* prefix_start;
   const int32_t* prefix_len;
-  float2* part_ml;   // [unit][nsplit][kRows]
-  float* part_acc;   // [unit][nsplit][kRows][D]
+  float2* part_ml;   // [lane][R + n_seq][kRows]
+  float* part_acc;   // [lane][R + n_seq][kRows][D]
+  int2* seg;         // [n_seq]: first and last range of each sequence
   uint16_t* o;
   float* lse;
-  int n_seq, blk_len, Hq, Hkv, G, rows, row_tiles, nsplit, chunk;
+  int n_seq, blk_len, Hq, Hkv, G, rows, row_tiles, R;
   float scale_log2;
 };
 
-// Copy this wave's share of the 32-key tile starting at key `key0` of the
-// sequence's key list (prefix rows of the cache, then the block's own rows) into
-// the swizzled LDS tile.  Keys >= kend are clamped to kend - 1.
+// Key tiles of sequence s: ceil((prefix_len + blk_len) / KT).
+__device__ __forceinline__ int seq_tiles(const DecParams& p, int s) {
+  return (p.prefix_len[s] + p.blk_len + KT - 1) / KT;
+}
+
+// A 64-bit value that is equal in every lane, made known to be wave-uniform.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Wave-level inclusive prefix sum (64 lanes).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Tiles of the line up to and including sequence c + lane, for the chunk of
+// 64 sequences starting at c (0 past the last sequence), and the chunk total.
+__device__ __forceinline__ int chunk_scan(const DecParams& p, int c, int lane, int& tiles, int& chunk_total) {
+  const int s = c + lane;
+  tiles = s < p.n_seq ? seq_tiles(p, s) : 0;
+  const int incl = wave_incl_scan(tiles, lane);
+  chunk_total = __shfl(incl, 63, 64);
+  return incl;
+}
+
+// The total number of tiles of the line, the first tile x of range r, and the
+// sequence s_at holding tile x with the number of tiles before it.  Every lane returns the same values.
+// With at most 64 sequences the prefix lengths are read once.
+__device__ void line_locate(const DecParams& p, int r, int lane, long long& total, long long& x, int& s_at,
+                            long long& before) {
+  int tiles0, tot0;
+  const int incl0 = chunk_scan(p, 0, lane, tiles0, tot0);
+  total = tot0;
+  for (int c = 64; c < p.n_seq; c += 64) {
+    int t, ct;
+    chunk_scan(p, c, lane, t, ct);
+    total += ct;
+  }
+  x = total * r / p.R;   // first tile of range r (ranges split the line evenly)
+  s_at = -1;
+  before = 0;
+  long long acc = 0;
+  for (int c = 0; c < p.n_seq; c += 64) {
+    int t, ct, incl;
+    if (c == 0) {
+      t = tiles0;
+      ct = tot0;
+      incl = incl0;
+    } else {
+      incl = chunk_scan(p, c, lane, t, ct);
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(c + lane < p.n_seq && acc + incl > x);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s_at = c + l;
+      before = acc + __shfl(incl, l, 64) - __shfl(t, l, 64);
+      break;
+    }
+    acc += ct;
+  }
+}
+
+// Copy this wave's share of the 32-key tile starting at key `key0` of sequence
+// n's key list (prefix rows of the cache, then the block's own rows) into the
+// swizzled LDS tile.  Keys >= kend are clamped to kend - 1.
 __device__ __forceinline__ void dec_tile_dma(uint32_t lds_tile, const uint16_t* cache, const uint16_t* blk,
                                              int64_t start, int P, int n, int kvh, int blk_len, int Hkv,
                                              int key0, int kend, int wave, int lane) {
@@ -82,63 +161,110 @@ __device__ __forceinline__ void dec_tile_dma(uint32_t lds_tile, const uint16_t* 
   }
 }
 
+// A position on the line: sequence s, its tile j, and that sequence's
+// prefix length, first cache row and tile count.
+struct Cursor {
+  int s, j, P, tiles;
+  int64_t start;
+};
+
 __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // Workgroup order: kv head fastest, then row tile, then split, then sequence.
-  // A cache row interleaves the kv heads, so the workgroups dispatched together
-  // fetch neighbouring pieces of the same rows.
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
   const int rt = bid % p.row_tiles;
-  bid /= p.row_tiles;
-  const int split = bid % p.nsplit;
-  const int n = bid / p.nsplit;
-  const int unit = (n * p.Hkv + kvh) * p.row_tiles + rt;
-
-  const int P = p.prefix_len[n];
-  const int64_t start = p.prefix_start[n];
-  const int total = P + p.blk_len;
-  const int k0 = split * p.chunk;
-  if (k0 >= total) return;
-  const int k1 = min(total, k0 + p.chunk);
-  const int ntiles = (k1 - k0 + KT - 1) / KT;
+  const int r = bid / p.row_tiles;
+  const int lane_id = rt * p.Hkv + kvh;        // which line
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
   const int col = lane & 15, g4 = lane >> 4;
   const int rloc = wave * 16 + col;            // row within the tile
-  const int r = rt * kRows + rloc;             // row within the unit: r = hl * blk_len + t
-  const bool rvalid = r < p.rows;
-  const int hl = rvalid ? r / p.blk_len : 0, tok = rvalid ? r % p.blk_len : 0;
-  const int hq = kvh * p.G + hl;
-
+  auto write_partial = [&](int s, float m, float l, const f32x4* oacc) {
+    const int64_t slot = ((int64_t)lane_id * (p.R + p.n_seq) + r + s) * kRows + rloc;
+    if (g4 == 0) p.part_ml[slot] = make_float2(m, l);
+    float* acc = p.part_acc + slot * D + 4 * g4;
 #pragma unroll
-  for (int s = 0; s < kNS - 1; ++s) {
-    if (s < ntiles) {
-      const uint32_t st = lds0 + s * kStageBytes;
-      dec_tile_dma(st, p.k_cache, p.k_blk, start, P, n, kvh, p.blk_len, p.Hkv, k0 + s * KT, k1, wave, lane);
-      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, start, P, n, kvh, p.blk_len, p.Hkv, k0 + s * KT, k1, wave,
-                   lane);
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<float4*>(acc + 16 * db) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+  };
+
+  // This workgroup's range [x0, x1) of the line.
+  long long total, x0, before;
+  int s0;
+  line_locate(p, r, lane, total, x0, s0, before);
+  total = uniform64(total);
+  x0 = uniform64(x0);
+  const long long x1 = total * (r + 1) / p.R;
+  s0 = __builtin_amdgcn_readfirstlane(s0);
+  before = uniform64(before);
+  if (x0 >= x1) {
+    // An empty range (the line is shorter than R) that falls inside a sequence
+    // lies between that sequence's first and last ranges: it leaves a neutral
+    // partial so the merge can take every range in between.
+    if (x0 > before) {
+      f32x4 zero[8];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) zero[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      write_partial(s0, kNegInf, 0.f, zero);
     }
+    return;
   }
+  const int n_tiles = (int)(x1 - x0);
 
-  bf16x8 qreg[4];
-  {
-    const uint16_t* qr = p.q_blk + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + 8 * g4;
+  auto cursor_at = [&](int s, int j) {   // wave-uniform: scalar loads
+    Cursor c;
+    c.s = __builtin_amdgcn_readfirstlane(s);
+    c.j = __builtin_amdgcn_readfirstlane(j);
+    c.P = p.prefix_len[s];
+    c.tiles = (c.P + p.blk_len + KT - 1) / KT;
+    c.start = p.prefix_start[s];
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.j == c.tiles && c.s + 1 < p.n_seq) c = cursor_at(c.s + 1, 0);
+  };
+
+  // loader: the next tile to copy.  A tile wholly inside the cache prefix is
+  // 32 consecutive cache rows: a uniform base plus fixed per-lane offsets.
+  const int64_t rs = (int64_t)p.Hkv * D;
+  uint32_t dma_off[KT / 4 / kNW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qreg[t] = as_bf16x8(rvalid ? ldg16(qr + 32 * t) : make_uint4(0, 0, 0, 0));
+  for (int i = 0; i < KT / 4 / kNW; ++i) {
+    const int nn = wave * (KT / 4 / kNW) + i;
+    const int rr = 4 * nn + (lane >> 4);
+    dma_off[i] = (uint32_t)((rr * rs + 8 * ((lane & 15) ^ tile_swz(rr))) * 2);
   }
-  vm_wait<0>();
-
-  f32x4 oacc[8];
+  Cursor ld = cursor_at(s0, (int)(x0 - before));
+  auto load = [&](int u) {
+    const uint32_t st = lds0 + (u % kNS) * kStageBytes;
+    const int key0 = ld.j * KT, kend = ld.P + p.blk_len;
+    if (key0 + KT <= ld.P) {
+      const int64_t row0 = (ld.start + key0) * rs + (int64_t)kvh * D;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_use = kNegInf, l_run = 0.f;
+      for (int i = 0; i < KT / 4 / kNW; ++i) {
+        const uint32_t dst = st + (wave * (KT / 4 / kNW) + i) * 1024;
+        lds_dma16_s(p.k_cache + row0, dma_off[i], dst);
+        lds_dma16_s(p.v_cache + row0, dma_off[i], dst + kTileBytes);
+      }
+    } else {
+      dec_tile_dma(st, p.k_cache, p.k_blk, ld.start, ld.P, ld.s, kvh, p.blk_len, p.Hkv, key0, kend, wave, lane);
+      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, ld.start, ld.P, ld.s, kvh, p.blk_len, p.Hkv, key0, kend,
+                   wave, lane);
+    }
+    advance(ld);
+  };
+  for (int u = 0; u < kNS - 1 && u < n_tiles; ++u) load(u);
+
+  const int row = rt * kRows + rloc;           // row within the line: row = hl * blk_len + t
+  const bool rvalid = row < p.rows;
+  const int hl = rvalid ? row / p.blk_len : 0, tok = rvalid ? row % p.blk_len : 0;
+  const int hq = kvh * p.G + hl;
   const float c2 = p.scale_log2;
-
   // A-operand row of 16-key block kb (0, 1) for lane row rho = col:
   //   key 8*(rho/4) + 4*kb + rho%4
   // so that accumulator entry i of lane (col, g4) in block kb holds key
@@ -146,163 +272,216 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   // the B-operand k-slice of the PV product over the tile's 32 keys.
   const int arow = 8 * (col >> 2) + (col & 3);
   constexpr int per_tile = 2 * (KT / 4 / kNW);
+  // LDS byte offsets within a tile: K row 4*kb + arow, chunk g4 (ds = 0); the
+  // two transposed V reads of d-block 0 (rows 8*g4 + 4*h + (lane%16)/4,
+  // columns 4*(lane%4) .. +3, as tile_read_t16).
+  uint32_t kbase[2], vbase[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) kbase[kb] = tile_off(4 * kb + arow, g4);
+  {
+    const int li = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int vr = 8 * g4 + 4 * h + (li >> 2);
+      const int d = 4 * (li & 3);
+      vbase[h] = tile_off(vr, d >> 3) + 2 * (d & 7);
+    }
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int pending = min(kNS - 2, ntiles - 1 - t);
+  Cursor cc = cursor_at(s0, (int)(x0 - before));   // the tile being multiplied
+  bf16x8 qreg[4];
+  f32x4 oacc[8];
+  float m_use = kNegInf, l_run = 0.f;
+  auto begin_segment = [&]() {
+    const uint16_t* qr = p.q_blk + (((int64_t)cc.s * p.blk_len + tok) * p.Hq + hq) * D + 8 * g4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qreg[t] = as_bf16x8(rvalid ? ldg16(qr + 32 * t) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_use = kNegInf;
+    l_run = 0.f;
+  };
+  auto end_segment = [&]() {
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    write_partial(cc.s, m_use, l_tot, oacc);
+    if (lane_id == 0 && tid == 0 && cc.j + 1 == cc.tiles) p.seg[cc.s].y = r;
+  };
+  if (lane_id == 0 && tid == 0 && cc.j == 0) p.seg[cc.s].x = r;
+  begin_segment();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int pending = min(kNS - 2, n_tiles - 1 - t);
     if (pending >= 3) vm_wait<3 * per_tile>();
     else if (pending == 2) vm_wait<2 * per_tile>();
     else if (pending == 1) vm_wait<per_tile>();
     else vm_wait<0>();
     __syncthreads();
-    if (t + kNS - 1 < ntiles) {
-      const uint32_t st = lds0 + ((t + kNS - 1) % kNS) * kStageBytes;
-      const int kn = k0 + (t + kNS - 1) * KT;
-      dec_tile_dma(st, p.k_cache, p.k_blk, start, P, n, kvh, p.blk_len, p.Hkv, kn, k1, wave, lane);
-      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, start, P, n, kvh, p.blk_len, p.Hkv, kn, k1, wave, lane);
-    }
-    const int key0 = k0 + t * KT;
+    if (t + kNS - 1 < n_tiles) load(t + kNS - 1);
+    const int key0 = cc.j * KT;
+    const int kend = cc.P + p.blk_len;
     const uint32_t Kt = lds0 + (t % kNS) * kStageBytes;
     const uint32_t Vt = Kt + kTileBytes;
 
-    f32x4 sacc[2];
+    // All operand reads of the tile first (V's do not depend on the softmax):
+    // K rows 4*kb + arow at logical chunk 4*ds + g4, and V^T for d-block db by
+    // two transposed reads.  The swizzle touches only chunk bits, so each
+    // address is a per-lane base XOR a compile-time constant.
+    bf16x8 kop[8], vop[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = 4 * kb + arow;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        sacc[kb] = mfma_16x16x32(lds_read_b128(Kt + tile_off(row, 4 * ds + g4)), qreg[ds], sacc[kb]);
-    }
-    float mx = kNegInf;
-    if (key0 + KT > k1) {
+      for (int ds = 0; ds < 4; ++ds) kop[4 * kb + ds] = lds_read_b128(Kt + (kbase[kb] ^ (uint32_t)(ds << 6)));
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vop[db] = cat_i16x4(lds_read_tr16(Vt + (vbase[0] ^ (uint32_t)(db << 5))),
+                          lds_read_tr16(Vt + (vbase[1] ^ (uint32_t)(db << 5))));
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_16x16x32(kop[4 * kb + ds], qreg[ds], sacc[kb]);
+    if (key0 + KT > kend) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 8 * g4 + 4 * kb + i;
-          if (key >= k1) sacc[kb][i] = kNegInf;
-          mx = fmaxf(mx, sacc[kb][i]);
-        }
-    } else {
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 8 * g4 + 4 * kb + i >= kend) sacc[kb][i] = kNegInf;
+    }
+    // P = exp2(S * scale * log2 e - m_use).  The offset m_use is raised (with
+    // the matching rescale of O and l) only when this lane's exponentials
+    // would exceed 2^16, or while it is still -inf (the segment's first tile);
+    // O and l always share it, so the result is exact up to rounding.
+    auto exp8 = [&](float nm, float* pv) {
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = exp2_fast(__builtin_fmaf(sacc[0][i], c2, nm));
+        pv[4 + i] = exp2_fast(__builtin_fmaf(sacc[1][i], c2, nm));
+        ps += pv[i] + pv[4 + i];
+      }
+      return ps;
+    };
+    float pv[8];
+    float psum = exp8(-m_use, pv);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= 65536.0f))) {
+      float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    const bool grow = mx > m_use + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_use;
-      const float alpha = exp2_fast(m_use - m_new);
-      m_use = m_new;
-      l_run *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;   // the query row's maximum (its 4 lanes)
+      if (mx > m_use) {
+        const float alpha = exp2_fast(m_use - mx);   // 0 while m_use is -inf
+        m_use = mx;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
-    }
-    const float nm = -m_use;
-    float psum = 0.f;
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = exp2_fast(__builtin_fmaf(sacc[0][i], c2, nm));
-      pv[4 + i] = exp2_fast(__builtin_fmaf(sacc[1][i], c2, nm));
-      psum += pv[i] + pv[4 + i];
+        for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      }
+      psum = exp8(m_use == kNegInf ? 0.f : -m_use, pv);
     }
     const bf16x8 pb = pack_bf16x8(pv);
     l_run += psum;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = mfma_16x16x32(tile_read_t16(Vt, db, 0, lane), pb, oacc[db]);
-  }
+    for (int db = 0; db < 8; ++db) oacc[db] = mfma_16x16x32(vop[db], pb, oacc[db]);
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const int64_t slot = ((int64_t)unit * p.nsplit + split) * kRows + rloc;
-  if (g4 == 0) p.part_ml[slot] = make_float2(m_use, l_tot);
-  float* acc = p.part_acc + slot * D + 4 * g4;
-#pragma unroll
-  for (int db = 0; db < 8; ++db)
-    *reinterpret_cast<float4*>(acc + 16 * db) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+    // end of this sequence's segment: write its partial, move on
+    const bool seq_done = cc.j + 1 == cc.tiles;
+    if (seq_done || t + 1 == n_tiles) {
+      end_segment();
+      if (t + 1 < n_tiles) {
+        cc = cursor_at(cc.s + 1, 0);
+        if (lane_id == 0 && tid == 0) p.seg[cc.s].x = r;
+        begin_segment();
+      }
+    } else {
+      ++cc.j;
+    }
+  }
 }
 
-// 128 threads per query row, one head-dim entry each; kMergeRows rows per workgroup.
-__global__ __launch_bounds__(128 * kMergeRows) void decode_merge(DecParams p) {
-  const int per_unit = kRows / kMergeRows;
-  const int unit = blockIdx.x / per_unit;
-  const int rloc = (blockIdx.x % per_unit) * kMergeRows + threadIdx.x / D;
-  const int d = threadIdx.x % D;
-  const int rt = unit % p.row_tiles;
-  const int nk = unit / p.row_tiles;
-  const int kvh = nk % p.Hkv, n = nk / p.Hkv;
-  const int r = rt * kRows + rloc;
-  if (r >= p.rows) return;
-  const int total = p.prefix_len[n] + p.blk_len;
-  const int ns = min(p.nsplit, (total + p.chunk - 1) / p.chunk);
-  const int hl = r / p.blk_len, tok = r % p.blk_len;
+// 32 threads per query row, four head-dim entries each; kMergeRows rows per
+// workgroup.  One pass over the sequence's partials, up to kBatch of them per
+// round trip to memory, with a running maximum.
+__global__ __launch_bounds__(32 * kMergeRows) void decode_merge(DecParams p) {
+  constexpr int kRowGroups = kRows / kMergeRows;
+  const int unit = blockIdx.x / kRowGroups;      // (sequence, line)
+  const int rloc = (blockIdx.x % kRowGroups) * kMergeRows + threadIdx.x / 32;
+  const int d4 = threadIdx.x % 32;
+  const int lanes = p.row_tiles * p.Hkv;
+  const int lane_id = unit % lanes, n = unit / lanes;
+  const int kvh = lane_id % p.Hkv, rt = lane_id / p.Hkv;
+  const int row = rt * kRows + rloc;
+  if (row >= p.rows) return;
+  const int2 seg = p.seg[n];
+  const int ns = seg.y - seg.x + 1;              // ranges that met sequence n
+  const int hl = row / p.blk_len, tok = row % p.blk_len;
   const int hq = kvh * p.G + hl;
 
-  const int64_t base = (int64_t)unit * p.nsplit * kRows + rloc;
-  // Loads of up to kBatch splits are issued together (the split count is small
-  // but each load is a round trip to L2 / HBM).
+  const int64_t base = ((int64_t)lane_id * (p.R + p.n_seq) + seg.x + n) * kRows + rloc;
   constexpr int kBatch = 8;
-  float m = kNegInf;
-  for (int s0 = 0; s0 < ns; s0 += kBatch) {
-    float mb[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) mb[k] = (s0 + k < ns) ? p.part_ml[base + (int64_t)(s0 + k) * kRows].x : kNegInf;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) m = fmaxf(m, mb[k]);
-  }
-  float l = 0.f, acc = 0.f;
+  float m = kNegInf, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < ns; s0 += kBatch) {
     float2 ml[kBatch];
-    float a[kBatch];
+    float4 a[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int64_t slot = base + (int64_t)(s0 + k) * kRows;
       const bool ok = s0 + k < ns;
       ml[k] = ok ? p.part_ml[slot] : make_float2(kNegInf, 0.f);
-      a[k] = ok ? p.part_acc[slot * D + d] : 0.f;
+      a[k] = ok ? *reinterpret_cast<const float4*>(p.part_acc + slot * D + 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, ml[k].x);
+    const float r = m == kNegInf ? 0.f : exp2_fast(m - mb);   // rescale of what was summed so far
+    l *= r;
+    acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const float w = exp2_fast(ml[k].x - m);
+      const float w = ml[k].x == kNegInf ? 0.f : exp2_fast(ml[k].x - mb);
       l += ml[k].y * w;
-      acc += a[k] * w;
+      acc.x += a[k].x * w; acc.y += a[k].y * w; acc.z += a[k].z * w; acc.w += a[k].w * w;
     }
+    m = mb;
   }
-  const float o = acc / l;
-  const uint16_t ob = __builtin_bit_cast(uint16_t, (__bf16)o);
-  p.o[(((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + d] = ob;
-  if (p.lse && d == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
+  const float inv = 1.0f / l;
+  uint2 ob;
+  ob.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  ob.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(p.o + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + 4 * d4) = ob;
+  if (p.lse && d4 == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
 }
 
 struct Plan {
-  int row_tiles, nsplit, chunk;
-  long long units;
+  int row_tiles, lanes, R;
 };
 
 Plan make_plan(const DecodeShape& s) {
   Plan pl;
   const int rows = s.blk_len * (s.n_q_heads / s.n_kv_heads);
   pl.row_tiles = (rows + kRows - 1) / kRows;
-  pl.units = (long long)s.n_seq * s.n_kv_heads * pl.row_tiles;
-  const long long total_max = (long long)s.max_prefix_len + s.blk_len;
-  // Aim for about BD_DECODE_TARGET_WGS workgroups over the longest sequence's
-  // splits, with splits of at least four tiles (128 keys).
-  const long long want_splits = std::max<long long>(1, (BD_DECODE_TARGET_WGS + pl.units - 1) / pl.units);
-  long long chunk = (total_max + want_splits - 1) / want_splits;
-  chunk = std::max<long long>(4 * KT, ((chunk + KT - 1) / KT) * KT);
-  pl.chunk = (int)chunk;
-  pl.nsplit = (int)((total_max + chunk - 1) / chunk);
+  pl.lanes = s.n_kv_heads * pl.row_tiles;
+  // Tiles of the line when every prefix has the largest length (an upper
+  // bound: the ranges are cut from the actual line on the device).
+  const long long line_max = (long long)s.n_seq * (((long long)s.max_prefix_len + s.blk_len + KT - 1) / KT);
+  long long R = std::max<long long>(1, BD_DECODE_TARGET_WGS / pl.lanes);
+  R = std::min<long long>(R, std::max<long long>(1, line_max / kMinRangeTiles));
+  pl.R = (int)R;
   return pl;
+}
+
+size_t part_slots(const DecodeShape& s, const Plan& pl) {
+  return (size_t)pl.lanes * ((size_t)pl.R + s.n_seq) * kRows;
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(const DecodeShape& s, int /*is_bf16*/) {
   const Plan pl = make_plan(s);
-  return (size_t)pl.units * pl.nsplit * kRows * (sizeof(float2) + D * sizeof(float));
+  return part_slots(s, pl) * (sizeof(float2) + D * sizeof(float)) + (size_t)s.n_seq * sizeof(int2);
 }
 
 hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
@@ -316,6 +495,7 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   });
   if (attr_err != hipSuccess) return attr_err;
   const Plan pl = make_plan(s);
+  const size_t slots = part_slots(s, pl);
   DecParams p;
   p.q_blk = static_cast<const uint16_t*>(q_blk);
   p.k_blk = static_cast<const uint16_t*>(k_blk);
@@ -325,8 +505,8 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   p.prefix_start = prefix_start;
   p.prefix_len = prefix_len;
   p.part_ml = reinterpret_cast<float2*>(ws);
-  p.part_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                        (size_t)pl.units * pl.nsplit * kRows * sizeof(float2));
+  p.part_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + slots * sizeof(float2));
+  p.seg = reinterpret_cast<int2*>(reinterpret_cast<char*>(ws) + slots * (sizeof(float2) + D * sizeof(float)));
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.n_seq = s.n_seq;
@@ -336,14 +516,13 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   p.G = s.n_q_heads / s.n_kv_heads;
   p.rows = s.blk_len * p.G;
   p.row_tiles = pl.row_tiles;
-  p.nsplit = pl.nsplit;
-  p.chunk = pl.chunk;
+  p.R = pl.R;
   p.scale_log2 = s.scale * kLog2e;
-  hipLaunchKernelGGL(decode_split, dim3((unsigned)(pl.units * pl.nsplit)), dim3(kThreads), kSmemBytes, st, p);
+  hipLaunchKernelGGL(decode_split, dim3((unsigned)((long long)pl.R * pl.lanes)), dim3(kThreads), kSmemBytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge, dim3((unsigned)(pl.units * (kRows / kMergeRows))), dim3(128 * kMergeRows), 0, st,
-                     p);
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((long long)s.n_seq * pl.lanes * (kRows / kMergeRows))),
+                     dim3(32 * kMergeRows), 0, st, p);
   return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@
 // query i sees key j iff floor(j / L') <= floor(i / L'), i.e. j < key_limit(i).
 //
 // Work decomposition
-//   workgroup = NW waves = 32*NW consecutive query rows of one (batch, q head);
+//   workgroup = 8 waves = 256 consecutive query rows of one (batch, q head);
 //   each wave owns 32 rows.  The workgroup walks key tiles of 64 from key 0 to
 //   the largest key_limit of its rows, so tiles wholly in the future are never
 //   loaded or multiplied: cost follows the block mask (about L^2/2), not L^2.
@@ -14,24 +14,29 @@
 //   unmasked.
 //
 // Per wave and key tile (S^T formulation, see bd_device.hpp for layouts):
-//   S^T[64 keys x 32 q] = K Q^T   (2 x 8 MFMA 32x32x16; Q^T stays in registers,
+//   S^T[64 keys x 32 q] = K Q^T   (16 MFMA 32x32x16; Q^T stays in registers,
 //                                   K rows are read from LDS in sigma32 order)
-//   online softmax per query column (one cross-lane exchange per tile)
-//   O^T[128 d x 32 q] += V^T P^T   (4 x 4 MFMA 32x32x16; P^T comes straight
-//                                   from the S^T accumulator, V^T is read from
-//                                   the row-major V tile with transposed LDS
-//                                   reads)
-// K and V tiles go global -> LDS directly (no register staging) into a
-// two-stage ring of swizzled tiles: the next tile's loads are in flight while a
-// tile is multiplied; one barrier per tile.  Every LDS read address is a
-// per-lane register computed once plus a compile-time offset (the tile loop is
-// unrolled by the ring depth).
+//   softmax per query column
+//   O^T[128 d x 32 q] += V^T P^T   (16 MFMA 32x32x16; P^T comes straight from
+//                                   the S^T accumulator, V^T is read from the
+//                                   row-major V tile with transposed LDS reads)
+//
+// Two wave groups in antiphase ("ping-pong"): the two waves of each SIMD belong
+// to different groups.  Each tile takes two phases ended by workgroup
+// barriers; in every phase one group runs its matrix products (PV of the
+// previous tile interleaved with QK of this one, operands read a few products
+// ahead) while the other runs its softmax, so the SIMD's matrix pipe and vector
+// ALU work at the same time.  K and V tiles go global -> LDS directly into
+// three-stage rings of swizzled tiles; the loads are issued only by the group
+// that is in its softmax phase and waited for two phases later, so matrix
+// phases never wait on memory.
 //
 // Softmax: the score scale is folded into the exponent (one FMA per score
-// before exp2), and the running maximum used as the exponent offset is only
-// raised -- with the matching rescale of O and of the row sum -- when a
-// column's maximum grows by more than 2^8; exact either way, since O and the
-// row sum always share the same offset.
+// before exp2).  The exponent offset of a column is not its running maximum: it
+// is raised (with the matching rescale of O and of the row sum) only when a
+// tile's exponentials would exceed 2^16, which in practice happens only on a
+// column's first tile; O and the row sum always share the offset, so the result
+// is exact up to rounding.
 //
 // Workgroups of one (batch, kv head) are handed to the same XCD (L2 reuse of
 // K/V) and the most expensive query tiles are dispatched first.

@@ -159,6 +159,7 @@ def test_decode_step_workload():
     ([5, 300], 8, 4, 4),         # fewer rows than a row tile
     ([70, 2], 40, 8, 2),         # rows = 160: three row tiles
     ([4096 + 5], 32, 16, 8),
+    (list(range(0, 1500, 10)), 32, 16, 8),   # 150 sequences: the line scan spans several wave chunks
 ])
 def test_decode_ragged(plens, T, Hq, Hkv):
     banner(f"decode bf16 plens={plens} T={T} Hq={Hq} Hkv={Hkv}")
