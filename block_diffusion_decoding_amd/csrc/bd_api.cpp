@@ -149,7 +149,7 @@ bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void*
 
 size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab) {
   if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
-  return bd::commit_workspace_bytes(n_seq, blk_len, vocab, 1);
+  return bd::commit_workspace_bytes(n_seq, blk_len, vocab);
 }
 
 bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
@@ -163,8 +163,8 @@ bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq
   if (std::isnan(threshold)) return BD_ERR_VALUE;
   if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
   const long long rows = (long long)n_seq * blk_len;
-  if (rows * bd::commit_chunks_per_row(vocab, dtype == BD_BF16) > kMaxGrid) return BD_ERR_SHAPE;
-  const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab, dtype == BD_BF16);
+  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
+  const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold,
                    fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};

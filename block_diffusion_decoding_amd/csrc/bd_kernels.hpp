@@ -58,8 +58,8 @@ struct CommitArgs {
   int32_t* n_masked_left;
   void* ws;
 };
-int commit_chunks_per_row(int vocab, int is_bf16);
-size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab, int is_bf16);
+int commit_chunks_per_row(long long rows, int vocab);
+size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 
 constexpr int kCommitMaxBlock = 1024;  // largest blk_len the commit kernel takes

