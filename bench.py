@@ -138,12 +138,14 @@ def main():
     loop_state = {"step": 0}
 
     if args.traffic_probe:
-        # Counter runs (rocprofv3 --pmc) read per-dispatch HBM bytes of these kernels; a
-        # plain 1 GiB device copy gives the scale of each counter.
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        # Counter runs (rocprofv3 --pmc) read per-dispatch HBM bytes of these kernels.  The
+        # scale of each counter comes from a plain streaming kernel of known size that no other
+        # step launches: a bitwise NOT of 2^28 int32 (1 GiB read, 1 GiB written).
+        src = torch.empty(REF_COPY_BYTES // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
         del src, dst
         for _ in range(3):
             bd.bd_attn_fwd(q, k, v, blk, o=o, lse=lse)
@@ -351,6 +353,8 @@ def main():
 
 
 KERNEL_SRC = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
+REF_COPY_KERNEL = "bitwise_not_kernel"     # the counter-scale reference kernel of the traffic probe
+REF_COPY_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -414,17 +418,19 @@ def summarize(args):
         out.append("## counters (average per dispatch)")
         out.append(f"{'kernel':60s} " + " ".join(f"{c:>26s}" for c in names))
         for kname, d in sorted(pmc.items()):
+            if not kname:
+                continue
             out.append(f"{kname:60s} " + " ".join(f"{d[c][1]:26.6g}" if c in d else f"{'-':>26s}" for c in names))
-        copy = next((d for k, d in pmc.items() if "copyBuffer" in k), None)
+        copy = next((d for k, d in pmc.items() if REF_COPY_KERNEL in k), None)
         if copy and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
-            gib_kib = float(1 << 20)
-            ff, fw = gib_kib / copy["FETCH_SIZE"][1], gib_kib / copy["WRITE_SIZE"][1]
+            ref_kib = REF_COPY_BYTES / 1024.0
+            ff, fw = ref_kib / copy["FETCH_SIZE"][1], ref_kib / copy["WRITE_SIZE"][1]
             out.append("")
-            out.append(f"## HBM bytes per launch; counter scale from the 1 GiB reference copy: FETCH x{ff:.3f}, "
-                       f"WRITE x{fw:.3f}")
+            out.append(f"## HBM bytes per launch; counter scale from the reference kernel ({REF_COPY_KERNEL}, "
+                       f"{REF_COPY_BYTES} bytes read and written): FETCH x{ff:.3f}, WRITE x{fw:.3f}")
             out.append("# traffic <kernel> <read_bytes> <written_bytes> src=<kernel source hash>")
             for kname, d in sorted(pmc.items()):
-                if "FETCH_SIZE" in d and "WRITE_SIZE" in d and "copyBuffer" not in kname:
+                if "FETCH_SIZE" in d and "WRITE_SIZE" in d and REF_COPY_KERNEL not in kname and kname:
                     out.append(f"traffic {kname} {d['FETCH_SIZE'][1] * 1024 * ff:.0f} {d['WRITE_SIZE'][1] * 1024 * fw:.0f} "
                                f"src={kernel_source_hash()}")
     text = "\n".join(out) + "\n"

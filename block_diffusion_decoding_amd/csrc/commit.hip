@@ -3,12 +3,14 @@
 //
 // Two kernels on the caller's stream:
 //   1. commit_reduce: one workgroup per (masked row, vocabulary chunk) streams
-//      its chunk of logits from HBM once (16-byte loads, one step of loads in
-//      flight ahead of the arithmetic) and reduces it to (max, lowest argmax,
-//      sum exp(x - max), invalid flag).  Rows not masked on entry are skipped
-//      without touching their logits.  The chunk count per row is chosen so
-//      that about 2048 workgroups are launched: one per row when many rows
-//      are decoded together, many per row for a single block.
+//      its chunk of logits from HBM once (16-byte loads, several steps of
+//      loads in flight ahead of the arithmetic) and reduces it to (max, lowest
+//      argmax, sum exp(x - max), invalid flag).  Rows not masked on entry are
+//      skipped without touching their logits.  The chunk count per row is
+//      chosen so that about 8192 workgroups are launched: several per row even
+//      when many rows are decoded together, so that the few rows still masked
+//      late in a decode loop still spread over the whole chip, and many per
+//      row for a single block.
 //   2. commit_decide: one workgroup per block merges the chunk partials of its
 //      rows (associative merge: max, lowest id on ties, rescaled sums; eight
 //      threads per row), forms conf = 1 / sum, and applies the threshold /
@@ -19,13 +21,17 @@
 
 #include <algorithm>
 
+#ifndef BD_COMMIT_TARGET_WGS
+#define BD_COMMIT_TARGET_WGS 8192
+#endif
+
 namespace bd {
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStep = 2048;          // vocabulary entries per workgroup and load step (bf16)
-constexpr int kTargetWGs = 2048;     // workgroups the chunking aims for
+constexpr int kTargetWGs = BD_COMMIT_TARGET_WGS;   // workgroups the chunking aims for
 constexpr int kMinChunk = 4096;      // fewest vocabulary entries per chunk
 constexpr int kDecideLanes = 8;      // threads merging one row's partials
 
