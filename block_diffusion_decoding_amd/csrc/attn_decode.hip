@@ -13,9 +13,10 @@
 //   decode_split  workgroup = (range, row tile, kv head), kv head fastest so
 //                 that neighbouring workgroups read neighbouring pieces of the
 //                 same cache rows.  Four waves own 16 query rows each and share
-//                 K/V tiles copied global -> LDS directly into a ring of kNS
-//                 swizzled stages that runs on across sequence boundaries.  Per
-//                 tile and wave:
+//                 K/V tiles staged through registers into two swizzled LDS
+//                 stages (two tiles in flight in registers while one is
+//                 multiplied); the pipeline runs on across sequence
+//                 boundaries.  Per tile and wave:
 //                   S^T[32 keys x 16 q] = K Q^T  (2 x 4 MFMA 16x16x32)
 //                   O^T[128 d x 16 q]  += V^T P^T (8 MFMA 16x16x32, V^T read
 //                                                  transposed from LDS)
@@ -33,11 +34,8 @@
 #include <algorithm>
 #include <mutex>
 
-// Pipeline shape (compile-time): LDS ring depth, and the number of workgroups
-// the plan aims for (256 compute units x 3 resident workgroups of 48 KB LDS).
-#ifndef BD_DECODE_NS
-#define BD_DECODE_NS 3
-#endif
+// The number of workgroups the plan aims for (256 compute units x 3 resident
+// workgroups, a limit set by registers); a compile-time knob for tuning builds.
 #ifndef BD_DECODE_TARGET_WGS
 #define BD_DECODE_TARGET_WGS 768
 #endif
@@ -48,14 +46,25 @@ namespace {
 constexpr int D = 128;
 constexpr int KT = 32;
 constexpr int kNW = 4;
-constexpr int kNS = BD_DECODE_NS;
 constexpr int kThreads = kNW * 64;
 constexpr int kRows = 64;                     // query rows per workgroup (4 waves x 16)
 constexpr int kTileBytes = KT * D * 2;      // 8 KB
 constexpr int kStageBytes = 2 * kTileBytes;
-constexpr size_t kSmemBytes = (size_t)kNS * kStageBytes;
+constexpr size_t kSmemBytes = 2 * (size_t)kStageBytes;   // two stages
+constexpr int kPieces = KT / 4 / kNW;         // 16-byte pieces per thread per tile, of K and of V
+
+// One tile in flight in registers: this thread's pieces of K and of V.
+struct Staged {
+  uint4 k[kPieces], v[kPieces];
+};
+
+__device__ __forceinline__ void lds_write16(uint32_t lds_addr, const uint4& v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)lds_addr) = w;
+}
 constexpr int kMergeRows = 8;                 // query rows per merge workgroup
-constexpr int kMinRangeTiles = 2;             // fewest tiles per range the plan aims for
+constexpr int kMinRangeTiles = 8;             // fewest tiles per range the plan aims for
 
 struct DecParams {
   const uint16_t* q_blk;
@@ -143,24 +152,6 @@ __device__ void line_locate(const DecParams& p, int r, int lane, long long& tota
   }
 }
 
-// Copy this wave's share of the 32-key tile starting at key `key0` of sequence
-// n's key list (prefix rows of the cache, then the block's own rows) into the
-// swizzled LDS tile.  Keys >= kend are clamped to kend - 1.
-__device__ __forceinline__ void dec_tile_dma(uint32_t lds_tile, const uint16_t* cache, const uint16_t* blk,
-                                             int64_t start, int P, int n, int kvh, int blk_len, int Hkv,
-                                             int key0, int kend, int wave, int lane) {
-  const int64_t rs = (int64_t)Hkv * D;
-#pragma unroll
-  for (int i = 0; i < KT / 4 / kNW; ++i) {
-    const int nn = wave * (KT / 4 / kNW) + i;
-    const int r = 4 * nn + (lane >> 4);
-    const int c = (lane & 15) ^ tile_swz(r);
-    const int j = min(key0 + r, kend - 1);
-    const uint16_t* src = j < P ? cache + (start + j) * rs : blk + ((int64_t)n * blk_len + (j - P)) * rs;
-    lds_dma16(src + kvh * D + 8 * c, lds_tile + nn * 1024);
-  }
-}
-
 // A position on the line: sequence s, its tile j, and that sequence's
 // prefix length, first cache row and tile count.
 struct Cursor {
@@ -168,7 +159,7 @@ struct Cursor {
   int64_t start;
 };
 
-__global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -216,49 +207,79 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   }
   const int n_tiles = (int)(x1 - x0);
 
-  auto cursor_at = [&](int s, int j) {   // wave-uniform: scalar loads
+  // Wave-uniform: read through the constant address space, so the loads are
+  // scalar and tracked by lgkmcnt, not by the vmcnt that the tile copies use.
+  typedef __attribute__((address_space(4))) const int32_t c_i32;
+  typedef __attribute__((address_space(4))) const int64_t c_i64;
+  auto cursor_at = [&](int s, int j) {
     Cursor c;
     c.s = __builtin_amdgcn_readfirstlane(s);
     c.j = __builtin_amdgcn_readfirstlane(j);
-    c.P = p.prefix_len[s];
+    c.P = ((c_i32*)(uintptr_t)p.prefix_len)[c.s];
     c.tiles = (c.P + p.blk_len + KT - 1) / KT;
-    c.start = p.prefix_start[s];
+    c.start = ((c_i64*)(uintptr_t)p.prefix_start)[c.s];
     return c;
   };
   auto advance = [&](Cursor& c) {
     if (++c.j == c.tiles && c.s + 1 < p.n_seq) c = cursor_at(c.s + 1, 0);
   };
 
-  // loader: the next tile to copy.  A tile wholly inside the cache prefix is
-  // 32 consecutive cache rows: a uniform base plus fixed per-lane offsets.
+  // Loader: register-staged copies.  fetch() reads the next tile of the line
+  // (cursor ld) into registers: each thread its two 16-byte pieces of K and of
+  // V (rows 4*nn + lane/16 of the tile, logical chunk (lane%16) ^ swizzle);
+  // put() writes them to an LDS stage at the swizzled positions.  A tile
+  // wholly inside the cache prefix is 32 consecutive cache rows: a uniform
+  // base plus fixed per-lane offsets.  (Measured on gfx950, this path streams
+  // HBM at about 6.8 TB/s where global -> LDS copies reach about 6.0.)
   const int64_t rs = (int64_t)p.Hkv * D;
-  uint32_t dma_off[KT / 4 / kNW];
+  uint32_t row_off[kPieces];
 #pragma unroll
-  for (int i = 0; i < KT / 4 / kNW; ++i) {
-    const int nn = wave * (KT / 4 / kNW) + i;
+  for (int i = 0; i < kPieces; ++i) {
+    const int nn = wave * kPieces + i;
     const int rr = 4 * nn + (lane >> 4);
-    dma_off[i] = (uint32_t)((rr * rs + 8 * ((lane & 15) ^ tile_swz(rr))) * 2);
+    row_off[i] = (uint32_t)((rr * rs + 8 * ((lane & 15) ^ tile_swz(rr))) * 2);
   }
   Cursor ld = cursor_at(s0, (int)(x0 - before));
-  auto load = [&](int u) {
-    const uint32_t st = lds0 + (u % kNS) * kStageBytes;
+  // Every step issues exactly one fetch (past the range it repeats the last
+  // tile, an L2 hit, without moving the cursor): with a fixed number of loads
+  // between a fetch and its put, the compiler waits for just that fetch.
+  auto fetch = [&](Staged& sg, bool adv) __attribute__((always_inline)) {
     const int key0 = ld.j * KT, kend = ld.P + p.blk_len;
     if (key0 + KT <= ld.P) {
       const int64_t row0 = (ld.start + key0) * rs + (int64_t)kvh * D;
+      const char* kg = reinterpret_cast<const char*>(p.k_cache + row0);
+      const char* vg = reinterpret_cast<const char*>(p.v_cache + row0);
 #pragma unroll
-      for (int i = 0; i < KT / 4 / kNW; ++i) {
-        const uint32_t dst = st + (wave * (KT / 4 / kNW) + i) * 1024;
-        lds_dma16_s(p.k_cache + row0, dma_off[i], dst);
-        lds_dma16_s(p.v_cache + row0, dma_off[i], dst + kTileBytes);
+      for (int i = 0; i < kPieces; ++i) {
+        sg.k[i] = ldg16(kg + row_off[i]);
+        sg.v[i] = ldg16(vg + row_off[i]);
       }
     } else {
-      dec_tile_dma(st, p.k_cache, p.k_blk, ld.start, ld.P, ld.s, kvh, p.blk_len, p.Hkv, key0, kend, wave, lane);
-      dec_tile_dma(st + kTileBytes, p.v_cache, p.v_blk, ld.start, ld.P, ld.s, kvh, p.blk_len, p.Hkv, key0, kend,
-                   wave, lane);
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int nn = wave * kPieces + i;
+        const int rr = 4 * nn + (lane >> 4);
+        const int c = (lane & 15) ^ tile_swz(rr);
+        const int j = min(key0 + rr, kend - 1);
+        const int64_t grow = j < ld.P ? (ld.start + j) : -1;
+        const int64_t brow = ((int64_t)ld.s * p.blk_len + (j - ld.P));
+        const uint16_t* ksrc = (grow >= 0 ? p.k_cache + grow * rs : p.k_blk + brow * rs) + kvh * D + 8 * c;
+        const uint16_t* vsrc = (grow >= 0 ? p.v_cache + grow * rs : p.v_blk + brow * rs) + kvh * D + 8 * c;
+        sg.k[i] = ldg16(ksrc);
+        sg.v[i] = ldg16(vsrc);
+      }
     }
-    advance(ld);
+    if (adv) advance(ld);
   };
-  for (int u = 0; u < kNS - 1 && u < n_tiles; ++u) load(u);
+  auto put = [&](const Staged& sg, int stage) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + stage * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const uint32_t dst = st + (wave * kPieces + i) * 1024 + lane * 16;
+      lds_write16(dst, sg.k[i]);
+      lds_write16(dst + kTileBytes, sg.v[i]);
+    }
+  };
 
   const int row = rt * kRows + rloc;           // row within the line: row = hl * blk_len + t
   const bool rvalid = row < p.rows;
@@ -271,7 +292,6 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   //   8*g4 + 4*kb + i,
   // the B-operand k-slice of the PV product over the tile's 32 keys.
   const int arow = 8 * (col >> 2) + (col & 3);
-  constexpr int per_tile = 2 * (KT / 4 / kNW);
   // LDS byte offsets within a tile: K row 4*kb + arow, chunk g4 (ds = 0); the
   // two transposed V reads of d-block 0 (rows 8*g4 + 4*h + (lane%16)/4,
   // columns 4*(lane%4) .. +3, as tile_read_t16).
@@ -292,10 +312,14 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   bf16x8 qreg[4];
   f32x4 oacc[8];
   float m_use = kNegInf, l_run = 0.f;
+  // The Q loads of a segment are waited for here, once per segment.  Left to
+  // itself the compiler would instead wait for them (vmcnt(0), which also
+  // covers the tile copies in flight) before the first product of every tile.
   auto begin_segment = [&]() {
     const uint16_t* qr = p.q_blk + (((int64_t)cc.s * p.blk_len + tok) * p.Hq + hq) * D + 8 * g4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) qreg[t] = as_bf16x8(rvalid ? ldg16(qr + 32 * t) : make_uint4(0, 0, 0, 0));
+    vm_wait<0>();
 #pragma unroll
     for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_use = kNegInf;
@@ -310,17 +334,23 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
   if (lane_id == 0 && tid == 0 && cc.j == 0) p.seg[cc.s].x = r;
   begin_segment();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int pending = min(kNS - 2, n_tiles - 1 - t);
-    if (pending >= 3) vm_wait<3 * per_tile>();
-    else if (pending == 2) vm_wait<2 * per_tile>();
-    else if (pending == 1) vm_wait<per_tile>();
-    else vm_wait<0>();
+  // Pipeline: tile t is multiplied from LDS stage t % 2 while tiles t+1 and
+  // t+2 are in flight in the register buffers (tile u in buffer u % 2).  After
+  // the products of tile t, tile t+1 goes to stage (t+1) % 2 (free: its
+  // previous tile was multiplied before this step's barrier) and the buffer
+  // fetches tile t+3.  The loop is unrolled by two so that the buffers are
+  // addressed statically.
+  Staged sa, sb;
+  fetch(sa, n_tiles > 1);
+  fetch(sb, n_tiles > 2);
+  put(sa, 0);
+  fetch(sa, n_tiles > 3);
+
+  auto step = [&](int t, Staged& nxt) __attribute__((always_inline)) {
     __syncthreads();
-    if (t + kNS - 1 < n_tiles) load(t + kNS - 1);
     const int key0 = cc.j * KT;
     const int kend = cc.P + p.blk_len;
-    const uint32_t Kt = lds0 + (t % kNS) * kStageBytes;
+    const uint32_t Kt = lds0 + (t & 1) * kStageBytes;
     const uint32_t Vt = Kt + kTileBytes;
 
     // All operand reads of the tile first (V's do not depend on the softmax):
@@ -332,10 +362,6 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) kop[4 * kb + ds] = lds_read_b128(Kt + (kbase[kb] ^ (uint32_t)(ds << 6)));
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      vop[db] = cat_i16x4(lds_read_tr16(Vt + (vbase[0] ^ (uint32_t)(db << 5))),
-                          lds_read_tr16(Vt + (vbase[1] ^ (uint32_t)(db << 5))));
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
@@ -384,7 +410,14 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
     const bf16x8 pb = pack_bf16x8(pv);
     l_run += psum;
 #pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vop[db] = cat_i16x4(lds_read_tr16(Vt + (vbase[0] ^ (uint32_t)(db << 5))),
+                          lds_read_tr16(Vt + (vbase[1] ^ (uint32_t)(db << 5))));
+#pragma unroll
     for (int db = 0; db < 8; ++db) oacc[db] = mfma_16x16x32(vop[db], pb, oacc[db]);
+
+    put(nxt, (t + 1) & 1);   // past the range: an unused copy into a stage nobody reads again
+    fetch(nxt, t + 4 < n_tiles);
 
     // end of this sequence's segment: write its partial, move on
     const bool seq_done = cc.j + 1 == cc.tiles;
@@ -398,7 +431,15 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecParams p) {
     } else {
       ++cc.j;
     }
+  };
+  // Whole pairs in the loop (both buffers fetched on every path to the back
+  // edge, so the compiler's waits before each put cover just that buffer).
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sb);
+    step(t + 1, sa);
   }
+  if (t < n_tiles) step(t, sb);
 }
 
 // 32 threads per query row, four head-dim entries each; kMergeRows rows per

@@ -194,9 +194,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   // The products of a matrix phase, interleaved: PV product i (d-block i%4,
   // k-step i/4) and QK product i (key block i%2, d-step i/2) alternate, so
   // products into the same accumulator are 4 to 8 apart, and the operands of
-  // the next kLook steps are read from LDS while a step is multiplied.
+  // the next kLook steps are read from LDS while a step is multiplied.  Two
+  // steps (128 matrix-pipe cycles) of lookahead measured faster than four or
+  // six: more reads in flight only back up the LDS queue that the matrix wave
+  // issues into.
   auto mm = [&]() __attribute__((always_inline)) {
-    constexpr int kLook = 4;
+    constexpr int kLook = 2;
     bf16x8 vop[16], kop[16];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
