@@ -53,6 +53,12 @@ constexpr int kStageBytes = 2 * kTileBytes;
 constexpr size_t kSmemBytes = 2 * (size_t)kStageBytes;   // two stages
 constexpr int kPieces = KT / 4 / kNW;         // 16-byte pieces per thread per tile, of K and of V
 
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One tile in flight in registers: this thread's pieces of K and of V.
 struct Staged {
   uint4 k[kPieces], v[kPieces];
@@ -251,8 +257,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const char* vg = reinterpret_cast<const char*>(p.v_cache + row0);
 #pragma unroll
       for (int i = 0; i < kPieces; ++i) {
-        sg.k[i] = ldg16(kg + row_off[i]);
-        sg.v[i] = ldg16(vg + row_off[i]);
+        sg.k[i] = ldg16_nt(kg + row_off[i]);
+        sg.v[i] = ldg16_nt(vg + row_off[i]);
       }
     } else {
 #pragma unroll
@@ -265,8 +271,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int64_t brow = ((int64_t)ld.s * p.blk_len + (j - ld.P));
         const uint16_t* ksrc = (grow >= 0 ? p.k_cache + grow * rs : p.k_blk + brow * rs) + kvh * D + 8 * c;
         const uint16_t* vsrc = (grow >= 0 ? p.v_cache + grow * rs : p.v_blk + brow * rs) + kvh * D + 8 * c;
-        sg.k[i] = ldg16(ksrc);
-        sg.v[i] = ldg16(vsrc);
+        sg.k[i] = ldg16_nt(ksrc);
+        sg.v[i] = ldg16_nt(vsrc);
       }
     }
     if (adv) advance(ld);
