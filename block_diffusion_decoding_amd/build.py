@@ -29,7 +29,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 SOURCES = ["bd_api.cpp", "commit.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip"]
 # The decode kernel keeps its matrix accumulators in ordinary VGPRs (otherwise
 # the compiler parks them in AGPRs and copies them back and forth every tile).
-PER_FILE = {"attn_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
+PER_FILE = {"attn_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
+            "attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, verbose: bool, build_dir: str, defines: dict) -> str:
