@@ -20,13 +20,16 @@
 //                   S^T[32 keys x 16 q] = K Q^T  (2 x 4 MFMA 16x16x32)
 //                   O^T[128 d x 16 q]  += V^T P^T (8 MFMA 16x16x32, V^T read
 //                                                  transposed from LDS)
-//                 At the end of each sequence's segment of the range it writes
-//                 the unnormalised partial state (m, l, acc) in fp32 to slot
-//                 range + sequence (distinct for every pair a range meets).
-//   decode_merge  combines the partials of each sequence exactly:
-//                 m = max m_s, l = sum l_s 2^(m_s - m),
-//                 O = sum acc_s 2^(m_s - m) / l, and writes O (bf16) and LSE;
-//                 32 threads per query row, four head-dim entries each.
+//                 A sequence that lies wholly inside the range gets its final
+//                 rows (O, LSE) directly; any other segment of the range
+//                 leaves a partial in slot range + sequence (distinct for
+//                 every pair a range meets): (m, l) in fp32 and O / l in bf16.
+//                 Outputs of segments that end inside the range wait in LDS
+//                 and are stored after the streaming loop.
+//   decode_merge  combines the partials of each sequence met by several
+//                 ranges: m = max m_s, w_s = l_s 2^(m_s - m),
+//                 O = sum w_s O_s / sum w_s, LSE = (m + log2 sum w_s) ln 2, in
+//                 fp32 (exact but for the bf16 rounding of each O_s).
 // Each K/V byte of the cache is read from HBM once per step.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
@@ -50,7 +53,8 @@ constexpr int kThreads = kNW * 64;
 constexpr int kRows = 64;                     // query rows per workgroup (4 waves x 16)
 constexpr int kTileBytes = KT * D * 2;      // 8 KB
 constexpr int kStageBytes = 2 * kTileBytes;
-constexpr size_t kSmemBytes = 2 * (size_t)kStageBytes;   // two stages
+constexpr int kStashBytes = 16 * D * 2 + 16 * 8;           // per wave: 16 rows of bf16 O, (m, l)
+constexpr size_t kSmemBytes = 2 * (size_t)kStageBytes + kNW * kStashBytes;   // two stages, the stash
 constexpr int kPieces = KT / 4 / kNW;         // 16-byte pieces per thread per tile, of K and of V
 
 __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
@@ -58,6 +62,8 @@ __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // One tile in flight in registers: this thread's pieces of K and of V.
 struct Staged {
@@ -69,7 +75,6 @@ __device__ __forceinline__ void lds_write16(uint32_t lds_addr, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)lds_addr) = w;
 }
-constexpr int kMergeRows = 8;                 // query rows per merge workgroup
 constexpr int kMinRangeTiles = 8;             // fewest tiles per range the plan aims for
 
 struct DecParams {
@@ -80,9 +85,8 @@ struct DecParams {
   const uint16_t* v_cache;
   const int64_t* prefix_start;
   const int32_t* prefix_len;
-  float2* part_ml;   // [lane][R + n_seq][kRows]
-  float* part_acc;   // [lane][R + n_seq][kRows][D]
-  int2* seg;         // [n_seq]: first and last range of each sequence
+  float2* part_ml;   // [lane][R + n_seq][kRows]: (m, l) of each partial row
+  uint16_t* part_o;  // [lane][R + n_seq][wave][dp][lane of wave][8]: bf16 O / l of each partial
   uint16_t* o;
   float* lse;
   int n_seq, blk_len, Hq, Hkv, G, rows, row_tiles, R;
@@ -181,14 +185,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   const int col = lane & 15, g4 = lane >> 4;
   const int rloc = wave * 16 + col;            // row within the tile
-  auto write_partial = [&](int s, float m, float l, const f32x4* oacc) {
-    const int64_t slot = ((int64_t)lane_id * (p.R + p.n_seq) + r + s) * kRows + rloc;
-    if (g4 == 0) p.part_ml[slot] = make_float2(m, l);
-    float* acc = p.part_acc + slot * D + 4 * g4;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<float4*>(acc + 16 * db) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
-  };
+  // partial slot of sequence s met by this range (distinct for every pair)
+  auto slot_of = [&](int s) { return (int64_t)lane_id * (p.R + p.n_seq) + r + s; };
 
   // This workgroup's range [x0, x1) of the line.
   long long total, x0, before;
@@ -203,12 +201,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // An empty range (the line is shorter than R) that falls inside a sequence
     // lies between that sequence's first and last ranges: it leaves a neutral
     // partial so the merge can take every range in between.
-    if (x0 > before) {
-      f32x4 zero[8];
-#pragma unroll
-      for (int db = 0; db < 8; ++db) zero[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      write_partial(s0, kNegInf, 0.f, zero);
-    }
+    if (x0 > before && g4 == 0) p.part_ml[slot_of(s0) * kRows + rloc] = make_float2(kNegInf, 0.f);
     return;
   }
   const int n_tiles = (int)(x1 - x0);
@@ -331,13 +324,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     m_use = kNegInf;
     l_run = 0.f;
   };
-  auto end_segment = [&]() {
+  // Segment outputs.  A sequence that lies wholly inside this range gets its
+  // final rows (O in bf16 and LSE); otherwise the segment leaves a partial:
+  // (m, l) in fp32 and O / l in bf16.  Lane (c, g4) holds rows' entries
+  // d = 16 db + 4 g4 + i; packed per pair of d-blocks into chunk dp, element e
+  // = d-block 2 dp + e / 4, entry e % 4.
+  //
+  // A global store inside the streaming loop stalls it: vmcnt retires in
+  // order, and the next wait for a tile waits for the store to be
+  // acknowledged, which under the read stream is slow (measured: ≈ 60 µs on
+  // the 64-sequence step).  So the output of a segment that ends before the
+  // range does goes to this wave's LDS stash and reaches memory after the
+  // loop (a rarer second such segment is stored directly).
+  auto store_out = [&](int s, bool whole, float m, float l, const uint4* w) __attribute__((always_inline)) {
+    if (whole) {
+      if (!rvalid) return;
+      uint16_t* orow = p.o + (((int64_t)s * p.blk_len + tok) * p.Hq + hq) * D + 4 * g4;
+#pragma unroll
+      for (int dp = 0; dp < 4; ++dp) {
+        *reinterpret_cast<uint2*>(orow + 32 * dp) = make_uint2(w[dp].x, w[dp].y);
+        *reinterpret_cast<uint2*>(orow + 32 * dp + 16) = make_uint2(w[dp].z, w[dp].w);
+      }
+      if (p.lse && g4 == 0) p.lse[((int64_t)s * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
+    } else {
+      const int64_t slot = slot_of(s);
+      if (g4 == 0) p.part_ml[slot * kRows + rloc] = make_float2(m, l);
+      uint16_t* po = p.part_o + ((slot * kNW + wave) * 4) * 64 * 8 + lane * 8;
+#pragma unroll
+      for (int dp = 0; dp < 4; ++dp) stg16(po + dp * 64 * 8, w[dp]);
+    }
+  };
+  const uint32_t stash = lds0 + 2 * kStageBytes + wave * kStashBytes;
+  int st_s = -1;
+  bool st_whole = false;
+  bool seg_from0 = cc.j == 0;   // the current segment began at its sequence's first tile
+  auto end_segment = [&](bool last) __attribute__((always_inline)) {
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    write_partial(cc.s, m_use, l_tot, oacc);
-    if (lane_id == 0 && tid == 0 && cc.j + 1 == cc.tiles) p.seg[cc.s].y = r;
+    const bool whole = seg_from0 && cc.j + 1 == cc.tiles;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    uint4 w[4];
+#pragma unroll
+    for (int dp = 0; dp < 4; ++dp) {
+      const f32x4 a0 = oacc[2 * dp], a1 = oacc[2 * dp + 1];
+      w[dp] = make_uint4(pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                         pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv));
+    }
+    if (last || st_s >= 0) {
+      store_out(cc.s, whole, m_use, l_tot, w);
+    } else {
+#pragma unroll
+      for (int dp = 0; dp < 4; ++dp) lds_write16(stash + (dp * 64 + lane) * 16, w[dp]);
+      if (g4 == 0)
+        *reinterpret_cast<__attribute__((address_space(3))) f32x2*>((uintptr_t)(stash + 16 * D * 2 + col * 8)) =
+            f32x2{m_use, l_tot};
+      st_s = __builtin_amdgcn_readfirstlane(cc.s);
+      st_whole = whole;
+    }
   };
-  if (lane_id == 0 && tid == 0 && cc.j == 0) p.seg[cc.s].x = r;
   begin_segment();
 
   // Pipeline: tile t is multiplied from LDS stage t % 2 while tiles t+1 and
@@ -428,10 +472,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // end of this sequence's segment: write its partial, move on
     const bool seq_done = cc.j + 1 == cc.tiles;
     if (seq_done || t + 1 == n_tiles) {
-      end_segment();
+      end_segment(t + 1 == n_tiles);
       if (t + 1 < n_tiles) {
         cc = cursor_at(cc.s + 1, 0);
-        if (lane_id == 0 && tid == 0) p.seg[cc.s].x = r;
+        seg_from0 = true;
         begin_segment();
       }
     } else {
@@ -446,60 +490,109 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     step(t + 1, sa);
   }
   if (t < n_tiles) step(t, sb);
+  if (st_s >= 0) {   // this wave's own stash: its LDS writes precede these reads
+    uint4 w[4];
+#pragma unroll
+    for (int dp = 0; dp < 4; ++dp) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)(stash + (dp * 64 + lane) * 16));
+      w[dp] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    const f32x2 ml = *reinterpret_cast<__attribute__((address_space(3))) f32x2*>((uintptr_t)(stash + 16 * D * 2 + col * 8));
+    store_out(st_s, st_whole, ml[0], ml[1], w);
+  }
 }
 
-// 32 threads per query row, four head-dim entries each; kMergeRows rows per
-// workgroup.  One pass over the sequence's partials, up to kBatch of them per
-// round trip to memory, with a running maximum.
-__global__ __launch_bounds__(32 * kMergeRows) void decode_merge(DecParams p) {
-  constexpr int kRowGroups = kRows / kMergeRows;
-  const int unit = blockIdx.x / kRowGroups;      // (sequence, line)
-  const int rloc = (blockIdx.x % kRowGroups) * kMergeRows + threadIdx.x / 32;
-  const int d4 = threadIdx.x % 32;
-  const int lanes = p.row_tiles * p.Hkv;
-  const int lane_id = unit % lanes, n = unit / lanes;
-  const int kvh = lane_id % p.Hkv, rt = lane_id / p.Hkv;
-  const int row = rt * kRows + rloc;
-  if (row >= p.rows) return;
-  const int2 seg = p.seg[n];
-  const int ns = seg.y - seg.x + 1;              // ranges that met sequence n
-  const int hl = row / p.blk_len, tok = row % p.blk_len;
-  const int hq = kvh * p.G + hl;
+// First tile and tile count of sequence n on the line, and the line's total.
+// Every lane returns the same values.
+__device__ void seq_span(const DecParams& p, int n, int lane, long long& total, long long& start, int& tiles_n) {
+  total = 0;
+  start = 0;
+  tiles_n = 0;
+  for (int c = 0; c < p.n_seq; c += 64) {
+    int t, ct;
+    const int incl = chunk_scan(p, c, lane, t, ct);
+    if (n >= c && n < c + 64) {
+      const int tn = __shfl(t, n - c, 64);
+      start = total + __shfl(incl, n - c, 64) - tn;
+      tiles_n = tn;
+    }
+    total += ct;
+  }
+}
 
-  const int64_t base = ((int64_t)lane_id * (p.R + p.n_seq) + seg.x + n) * kRows + rloc;
+// Merge: one workgroup per (sequence, line, block of 16 rows); thread
+// (dp = t / 64, l = t % 64) owns row 16 * block + l % 16 and the eight entries
+// of chunk dp.  The ranges that met sequence n are found from the same cut
+// points as in decode_split (range r starts at tile floor(total r / R)); a
+// sequence met by one range only was written whole there.  Otherwise
+//   m = max m_s,  w_s = l_s 2^(m_s - m),  O = sum w_s O_s / sum w_s,
+//   LSE = (m + log2 sum w_s) ln 2,
+// in one online pass in fp32 (O_s = the partial's O / l_s, stored in bf16;
+// ranges that are empty inside the sequence left l = 0 and are skipped).
+__global__ __launch_bounds__(256) void decode_merge(DecParams p) {
+  const int lanes = p.row_tiles * p.Hkv;
+  int u = blockIdx.x;
+  const int wb = u % kNW;
+  u /= kNW;
+  const int lane_id = u % lanes, n = u / lanes;
+  const int kvh = lane_id % p.Hkv, rt = lane_id / p.Hkv;
+  const int t = threadIdx.x, dp = t >> 6, ln = t & 63, col = ln & 15, g4 = ln >> 4;
+  const int rloc = wb * 16 + col;
+  const int row = rt * kRows + rloc;
+
+  long long total, start;
+  int tiles_n;
+  seq_span(p, n, ln, total, start, tiles_n);
+  if (tiles_n <= 0 || total <= 0) return;
+  const int r_first = (int)(((start + 1) * p.R - 1) / total);
+  const int r_last = (int)(((start + tiles_n) * p.R - 1) / total);
+  if (r_first == r_last || row >= p.rows) return;
+
+  // partials in batches of kBatch per round trip to memory
   constexpr int kBatch = 8;
-  float m = kNegInf, l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < ns; s0 += kBatch) {
-    float2 ml[kBatch];
-    float4 a[kBatch];
+  float m = kNegInf, lsum = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r0 = r_first; r0 <= r_last; r0 += kBatch) {
+    f32x2 ml[kBatch];
+    uint4 w[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int64_t slot = base + (int64_t)(s0 + k) * kRows;
-      const bool ok = s0 + k < ns;
-      ml[k] = ok ? p.part_ml[slot] : make_float2(kNegInf, 0.f);
-      a[k] = ok ? *reinterpret_cast<const float4*>(p.part_acc + slot * D + 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t slot = (int64_t)lane_id * (p.R + p.n_seq) + r0 + k + n;
+      const bool ok = r0 + k <= r_last;
+      const float2 v = ok ? p.part_ml[slot * kRows + rloc] : make_float2(kNegInf, 0.f);
+      ml[k] = f32x2{v.x, v.y};
+      w[k] = ok ? ldg16(p.part_o + ((slot * kNW + wb) * 4 + dp) * 64 * 8 + ln * 8) : make_uint4(0, 0, 0, 0);
     }
     float mb = m;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, ml[k].x);
-    const float r = m == kNegInf ? 0.f : exp2_fast(m - mb);   // rescale of what was summed so far
-    l *= r;
-    acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+    for (int k = 0; k < kBatch; ++k)
+      if (ml[k][1] > 0.f) mb = fmaxf(mb, ml[k][0]);
+    const float a = m == kNegInf ? 0.f : exp2_fast(m - mb);   // rescale of what was summed so far
+    lsum *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= a;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const float w = ml[k].x == kNegInf ? 0.f : exp2_fast(ml[k].x - mb);
-      l += ml[k].y * w;
-      acc.x += a[k].x * w; acc.y += a[k].y * w; acc.z += a[k].z * w; acc.w += a[k].w * w;
+      if (!(ml[k][1] > 0.f)) continue;   // empty ranges inside the sequence, and past the last
+      const float bw = ml[k][1] * exp2_fast(ml[k][0] - mb);
+      const uint32_t ww[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc[e] += bw * bf16_bits_to_f32((e & 1) ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xffffu);
+      lsum += bw;
     }
     m = mb;
   }
-  const float inv = 1.0f / l;
-  uint2 ob;
-  ob.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-  ob.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(p.o + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + 4 * d4) = ob;
-  if (p.lse && d4 == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(l)) * kLn2;
+  const float inv = 1.0f / lsum;
+  const int hl = row / p.blk_len, tok = row % p.blk_len;
+  const int hq = kvh * p.G + hl;
+  uint16_t* orow = p.o + (((int64_t)n * p.blk_len + tok) * p.Hq + hq) * D + 32 * dp + 4 * g4;
+  *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  *reinterpret_cast<uint2*>(orow + 16) =
+      make_uint2(pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  if (p.lse && dp == 0 && g4 == 0) p.lse[((int64_t)n * p.Hq + hq) * p.blk_len + tok] = (m + __log2f(lsum)) * kLn2;
 }
 
 struct Plan {
@@ -528,7 +621,7 @@ size_t part_slots(const DecodeShape& s, const Plan& pl) {
 
 size_t decode_workspace_bytes(const DecodeShape& s, int /*is_bf16*/) {
   const Plan pl = make_plan(s);
-  return part_slots(s, pl) * (sizeof(float2) + D * sizeof(float)) + (size_t)s.n_seq * sizeof(int2);
+  return part_slots(s, pl) * (sizeof(float2) + D * sizeof(uint16_t));
 }
 
 hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
@@ -552,8 +645,7 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   p.prefix_start = prefix_start;
   p.prefix_len = prefix_len;
   p.part_ml = reinterpret_cast<float2*>(ws);
-  p.part_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + slots * sizeof(float2));
-  p.seg = reinterpret_cast<int2*>(reinterpret_cast<char*>(ws) + slots * (sizeof(float2) + D * sizeof(float)));
+  p.part_o = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + slots * sizeof(float2));
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.n_seq = s.n_seq;
@@ -568,8 +660,7 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   hipLaunchKernelGGL(decode_split, dim3((unsigned)((long long)pl.R * pl.lanes)), dim3(kThreads), kSmemBytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((long long)s.n_seq * pl.lanes * (kRows / kMergeRows))),
-                     dim3(32 * kMergeRows), 0, st, p);
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((long long)s.n_seq * pl.lanes * kNW)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
