@@ -3,9 +3,9 @@
 //
 // Two kernels on the caller's stream:
 //   1. commit_reduce: one workgroup per (masked row, vocabulary chunk) streams
-//      its chunk of logits from HBM once (16-byte loads, several steps of
-//      loads in flight ahead of the arithmetic) and reduces it to (max, lowest
-//      argmax, sum exp(x - max), invalid flag).  Rows not masked on entry are
+//      its chunk of logits from HBM once (16-byte non-temporal loads, 64
+//      bytes per thread in flight ahead of the arithmetic) and reduces it to
+//      (max, lowest argmax, sum exp(x - max), invalid flag).  Rows not masked on entry are
 //      skipped without touching their logits.  The chunk count per row is
 //      chosen so that about 8192 workgroups are launched: several per row even
 //      when many rows are decoded together, so that the few rows still masked
@@ -84,8 +84,19 @@ template <> struct Vec<float> {
 // +Inf element makes m +Inf and s NaN; an element -Inf contributes 0.
 struct RowState {
   float m = kNegInf, s = 0.f;
+  float mb = 0.f;   // m * log2(e) once m is finite; 0 while m = -inf (then every exponent is -inf)
   int idx = 0x7fffffff, bad = 0;
 };
+
+// A new maximum mx > st.m at id: rescale the sum (a NaN summed so far is
+// recorded first, since the rescale by 0 could hide it).
+__device__ __forceinline__ void raise_max(RowState& st, float mx, int id) {
+  st.bad |= st.s != st.s;
+  st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - mx) * kLog2e);
+  st.m = mx;
+  st.mb = mx * kLog2e;
+  st.idx = id;
+}
 
 // Fold the N values starting at vocabulary id `base` (all valid).
 template <int N>
@@ -97,30 +108,22 @@ __device__ __forceinline__ void fold_vec(const float* x, int base, RowState& st)
     int j0 = N - 1;
 #pragma unroll
     for (int j = N - 2; j >= 0; --j) j0 = x[j] == vmax ? j : j0;
-    st.bad |= st.s != st.s;
-    st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - vmax) * kLog2e);
-    st.m = vmax;
-    st.idx = base + j0;
+    raise_max(st, vmax, base + j0);
   }
-  const float mb = st.m * kLog2e;
-  float a = 0.f, b = 0.f;
+  float e[N];
 #pragma unroll
-  for (int j = 0; j < N; j += 2) {
-    a += exp2_fast(__builtin_fmaf(x[j], kLog2e, -mb));
-    b += exp2_fast(__builtin_fmaf(x[j + 1], kLog2e, -mb));
-  }
-  st.s += a + b;
+  for (int j = 0; j < N; ++j) e[j] = exp2_fast(__builtin_fmaf(x[j], kLog2e, -st.mb));
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int j = 0; j < N; j += 2 * w) e[j] += e[j + w];
+  st.s += e[0];
 }
 
 // A single value (ragged tail / unaligned rows).
 __device__ __forceinline__ void fold_one(float x, int id, RowState& st) {
-  if (x > st.m) {
-    st.bad |= st.s != st.s;
-    st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - x) * kLog2e);
-    st.m = x;
-    st.idx = id;
-  }
-  st.s += exp2_fast(__builtin_fmaf(x, kLog2e, -st.m * kLog2e));
+  if (x > st.m) raise_max(st, x, id);
+  st.s += exp2_fast(__builtin_fmaf(x, kLog2e, -st.mb));
 }
 
 template <typename T, bool kVector>
@@ -139,31 +142,55 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
   RowState st;
   if (kVector) {
     constexpr int N = Vec<T>::N;
-    constexpr int kU = kStep / (N * kThreads);   // vectors per thread and step (bf16: 1, f32: 2)
-    constexpr int kAhead = 4;                    // steps of loads in flight
+    constexpr int kA = 32 / N;   // rounds of loads in flight (64 bytes per thread)
     typedef typename Vec<T>::Raw Raw;
     const int full = c0 + ((c1 - c0) / (N * kThreads)) * (N * kThreads);   // end of whole vector rounds
     const int nv = (full - c0) / (N * kThreads);                          // vector rounds in the chunk
-    Raw buf[kAhead * kU];
-    // prologue: the first kAhead steps' worth of vectors
+    const T* p = base + c0 + tid * N;
+    auto at = [&](int v) __attribute__((always_inline)) { return p + v * kThreads * N; };
+    auto fold = [&](const Raw& r, int v) __attribute__((always_inline)) {
+      float x[N];
+      Vec<T>::unpack(r, x);
+      fold_vec<N>(x, c0 + (v * kThreads + tid) * N, st);
+    };
+    Raw buf[kA];
+    if (nv >= 2 * kA) {
+      // Unconditional loads up to the end of the loop, so that the wait
+      // before each fold covers only the load it needs.
 #pragma unroll
-    for (int u = 0; u < kAhead * kU; ++u)
-      if (u < nv) buf[u] = Vec<T>::load(base + c0 + (u * kThreads + tid) * N);
-    for (int v0 = 0; v0 < nv; v0 += kAhead * kU) {
+      for (int u = 0; u < kA; ++u) buf[u] = Vec<T>::load(at(u));
+      int v0 = 0;
+      for (; v0 + 2 * kA <= nv; v0 += kA) {
 #pragma unroll
-      for (int u = 0; u < kAhead * kU; ++u) {
-        const int v = v0 + u;
-        if (v < nv) {
-          float x[N];
-          Vec<T>::unpack(buf[u], x);
-          if (v + kAhead * kU < nv) buf[u] = Vec<T>::load(base + c0 + ((v + kAhead * kU) * kThreads + tid) * N);
-          fold_vec<N>(x, c0 + (v * kThreads + tid) * N, st);
+        for (int u = 0; u < kA; ++u) {
+          fold(buf[u], v0 + u);
+          buf[u] = Vec<T>::load(at(v0 + u + kA));
         }
       }
+      // kA <= nv - v0 < 2 kA rounds left; buf holds rounds v0 .. v0 + kA - 1
+#pragma unroll
+      for (int u = 0; u < kA; ++u) {
+        fold(buf[u], v0 + u);
+        if (v0 + u + kA < nv) buf[u] = Vec<T>::load(at(v0 + u + kA));
+      }
+#pragma unroll
+      for (int u = 0; u < kA; ++u)
+        if (v0 + kA + u < nv) fold(buf[u], v0 + kA + u);
+    } else {
+      // a short chunk: at most two batches of kA rounds
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int u = 0; u < kA; ++u)
+          if (h * kA + u < nv) buf[u] = Vec<T>::load(at(h * kA + u));
+#pragma unroll
+        for (int u = 0; u < kA; ++u)
+          if (h * kA + u < nv) fold(buf[u], h * kA + u);
+      }
     }
-    for (int p = full + tid; p < c1; p += kThreads) fold_one(Vec<T>::scalar(base + p), p, st);
+    for (int q = full + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st);
   } else {
-    for (int p = c0 + tid; p < c1; p += kThreads) fold_one(Vec<T>::scalar(base + p), p, st);
+    for (int q = c0 + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st);
   }
   st.bad |= (st.s != st.s) | (st.m == __builtin_huge_valf());
 

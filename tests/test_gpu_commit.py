@@ -116,3 +116,47 @@ def test_batched_loop_scale():
     for T in wl.thresholds:
         near, amb, ref = run_case(bits, "bf16", tokens, masked, 32, T)
         print(f"  T={T} committed={int(ref['committed'].sum())} near={near} ambiguous={amb}")
+
+
+@pytest.mark.parametrize("n_masked", [1, 5, 37, 256])
+def test_few_masked_rows_in_large_batch(n_masked):
+    """A few masked rows among 256 rows of 151936 bf16 logits: the masked rows' logits are cut into
+    many short ranges (up to hundreds per row) whose partials the decide step merges; also every
+    row masked."""
+    banner(f"commit {n_masked} masked of 256 rows, V=151936")
+    rng = np.random.default_rng(100 + n_masked)
+    V, rows = 151936, 256
+    bits = W.boosted_logits_bits(rows, V, 2.0, 14.0, rng)
+    masked = np.zeros(rows, np.uint8)
+    masked[rng.choice(rows, n_masked, replace=False)] = 1
+    tokens = np.where(masked == 1, -1, 3).astype(np.int32)
+    for T in (0.5, 0.95):
+        near, amb, ref = run_case(bits, "bf16", tokens, masked, 32, T)
+        print(f"  T={T} committed={int(ref['committed'].sum())} near={near} ambiguous={amb}")
+
+
+def test_neg_inf_runs():
+    """-Inf logits in contiguous runs (a vocabulary mask): at the start of a row (whole load vectors
+    of -Inf before any finite value), in the middle and at the end; such rows are valid."""
+    banner("commit -inf runs")
+    rng = np.random.default_rng(21)
+    V, blk = 20011, 16
+    x = rng.standard_normal((2 * blk, V)).astype(np.float32)
+    x[0, :4096] = -np.inf
+    x[1, :8] = -np.inf
+    x[2, :7] = -np.inf
+    x[3, :2051] = -np.inf
+    x[4, 5000:9000] = -np.inf
+    x[5, V - 3000:] = -np.inf
+    x[6, :V - 1] = -np.inf               # one finite value, the last id: conf = 1
+    x[7, 1:] = -np.inf                   # one finite value, the first id
+    x[8, :] = -np.inf                    # all -inf: invalid
+    x[9, :10000] = -np.inf
+    x[9, 12345] = 9.0
+    bits = W.f32_to_bf16_bits(x)
+    masked = np.ones(2 * blk, np.uint8)
+    tokens = np.full(2 * blk, -1, np.int32)
+    for dt, arr in (("bf16", bits), ("f32", x)):
+        for T in (0.3, 0.9):
+            near, amb, ref = run_case(arr, dt, tokens, masked, blk, T)
+            assert np.isfinite(ref["conf"][[0, 1, 2, 3, 4, 5, 6, 7, 9]]).all()
