@@ -264,6 +264,22 @@ def main():
 
     loops = [full_loop(T) for T in lw.thresholds]
 
+    # per-position thresholds (bd_confidence_commit_rowwise) on the all-masked first step
+    thr_rows = torch.from_numpy(np.random.default_rng(lw.seed + 7).uniform(0.5, 0.99, n_rows)
+                                .astype(np.float32)).to(dev)
+    msk_rw = [torch.ones_like(masked) for _ in range(n_pool)]
+    rw_us = []
+    for rnd in range(4):
+        for m in msk_rw:
+            m.fill_(1)
+        t_us = primed([lambda i=i: bd.bd_confidence_commit(logit_pool[i], tokens, msk_rw[i], lw.block_size, thr_rows,
+                                                           conf=conf, pred=pred, n_committed=ncom,
+                                                           n_masked_left=nleft, workspace=com_ws)
+                       for i in range(n_pool)])
+        if rnd:
+            rw_us.extend(t_us)
+    rw_bytes = n_rows * V * 2
+
     # ------------------------------- single-shot decode step / commit, 4096 prefix
     sw = W.WORKLOADS["decode_step_bf16"]
     n_copies_kv, n_copies_lg = 40, 64
@@ -339,6 +355,7 @@ def main():
                         "attn_GBps": round(kv_bytes_loop / (np.median(dec_ms) * 1e-3) / 1e9, 1),
                         "commit_GBps_first_step": round(com_gbs_loop[0], 1),
                         "commit_GBps_median": round(float(np.median(com_gbs_loop)), 1),
+                        "commit_rowwise_GBps_first_step": round(rw_bytes / (np.median(rw_us) * 1e-6) / 1e9, 1),
                         "by_threshold": loops},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),

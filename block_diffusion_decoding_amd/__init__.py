@@ -17,6 +17,7 @@ from ._lib import (BD_BF16, BD_F32, BD_FALLBACK_NONE, BD_FALLBACK_TOP1, BdError,
 
 __all__ = [
     "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
+    "bd_confidence_commit_rowwise",
     "bd_attn_bwd_workspace_size", "bd_attn_decode_workspace_size", "bd_confidence_commit_workspace_size",
     "BdError", "BD_F32", "BD_BF16", "BD_FALLBACK_NONE", "BD_FALLBACK_TOP1", "lib",
 ]
@@ -139,13 +140,15 @@ def bd_confidence_commit_workspace_size(n_seq, blk_len, vocab) -> int:
     return int(lib.bd_confidence_commit_workspace_size(n_seq, blk_len, vocab))
 
 
-def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold: float, fallback: int = BD_FALLBACK_TOP1,
+def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold, fallback: int = BD_FALLBACK_TOP1,
                          vocab: Optional[int] = None, conf=None, pred=None, n_committed=None, n_masked_left=None,
                          want_rows: bool = True, workspace=None, stream=None):
     """Threshold commit; updates ``tokens``/``masked`` in place.
 
     logits [rows, >= vocab] (row stride = logits.stride(0)); tokens int32 [rows];
-    masked uint8 [rows].  Returns dict(conf, pred, n_committed, n_masked_left).
+    masked uint8 [rows]; ``threshold`` a number (every row) or a float32 device
+    tensor [rows] (one per row: ``bd_confidence_commit_rowwise``).  Returns
+    dict(conf, pred, n_committed, n_masked_left).
     """
     rows = logits.shape[0]
     if rows % blk_len:
@@ -163,8 +166,17 @@ def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold: float,
     n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
     n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
     ws, nb = _workspace(bd_confidence_commit_workspace_size(n_seq, blk_len, V), dev, workspace)
-    st = lib.bd_confidence_commit(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
-                                  float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred),
-                                  _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
-    check(st, "bd_confidence_commit")
+    if isinstance(threshold, torch.Tensor):
+        _need(threshold, "threshold", (rows,), torch.float32)
+        st = lib.bd_confidence_commit_rowwise(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
+                                              _ptr(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf),
+                                              _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb,
+                                              _stream(stream))
+        check(st, "bd_confidence_commit_rowwise")
+    else:
+        st = lib.bd_confidence_commit(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
+                                      float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf),
+                                      _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb,
+                                      _stream(stream))
+        check(st, "bd_confidence_commit")
     return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}

@@ -39,6 +39,25 @@ bd_status check_attn_shape(int batch, int seqlen, int hq, int hkv, int d, int bl
   return BD_OK;
 }
 
+bd_status commit_common(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab, bd_dtype dtype,
+                        float threshold, const float* thresholds, bd_fallback fallback, int32_t* tokens,
+                        uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
+                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !tokens || !masked) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || row_stride < vocab) return BD_ERR_SHAPE;
+  if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
+  if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
+  if (std::isnan(threshold)) return BD_ERR_VALUE;
+  if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
+  const long long rows = (long long)n_seq * blk_len;
+  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
+  const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, thresholds,
+                   fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
+  return hip_status(bd::launch_commit(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,19 +175,18 @@ bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq
                                bd_dtype dtype, float threshold, bd_fallback fallback, int32_t* tokens,
                                uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
                                int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!logits || !tokens || !masked) return BD_ERR_NULL;
-  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || row_stride < vocab) return BD_ERR_SHAPE;
-  if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
-  if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
-  if (std::isnan(threshold)) return BD_ERR_VALUE;
-  if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
-  const long long rows = (long long)n_seq * blk_len;
-  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
-  const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab);
-  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
-  bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold,
-                   fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
-  return hip_status(bd::launch_commit(a, stream));
+  return commit_common(logits, row_stride, n_seq, blk_len, vocab, dtype, threshold, nullptr, fallback, tokens,
+                       masked, conf, pred, n_committed, n_masked_left, workspace, ws_bytes, stream);
+}
+
+bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, const float* thresholds, bd_fallback fallback,
+                                       int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred,
+                                       int32_t* n_committed, int32_t* n_masked_left, void* workspace,
+                                       size_t ws_bytes, hipStream_t stream) {
+  if (!thresholds) return BD_ERR_NULL;
+  return commit_common(logits, row_stride, n_seq, blk_len, vocab, dtype, 0.f, thresholds, fallback, tokens,
+                       masked, conf, pred, n_committed, n_masked_left, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

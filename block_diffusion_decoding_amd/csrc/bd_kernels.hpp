@@ -49,6 +49,7 @@ struct CommitArgs {
   int n_seq, blk_len, vocab;
   int is_bf16;
   float threshold;
+  const float* thresholds;   // per row (device), or null: `threshold` for every row
   int fallback_top1;
   int32_t* tokens;
   uint8_t* masked;

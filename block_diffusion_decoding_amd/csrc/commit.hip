@@ -13,8 +13,8 @@
 //      row for a single block.
 //   2. commit_decide: one workgroup per block merges the chunk partials of its
 //      rows (associative merge: max, lowest id on ties, rescaled sums; eight
-//      threads per row), forms conf = 1 / sum, and applies the threshold /
-//      fallback rule.
+//      threads per row), forms conf = 1 / sum, and applies the threshold
+//      (one for every row, or one per row) and the fallback rule.
 // The HBM traffic is the logits of the masked rows plus a few bytes per row.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
@@ -221,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
 }
 
 __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restrict__ part, int nchunk,
-                                                          int blk_len, float threshold, int fallback_top1,
+                                                          int blk_len, float threshold,
+                                                          const float* __restrict__ thr_rows, int fallback_top1,
                                                           int32_t* __restrict__ tokens,
                                                           uint8_t* __restrict__ masked,
                                                           float* __restrict__ conf_out,
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
                                                           int32_t* __restrict__ n_left) {
   __shared__ float s_conf[kCommitMaxBlock];
   __shared__ int s_pred[kCommitMaxBlock];
+  __shared__ unsigned char s_pass[kCommitMaxBlock];
   __shared__ float s_best_c[kThreads / 64];
   __shared__ int s_best_r[kThreads / 64];
   const int g = blockIdx.x;
@@ -273,7 +275,9 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
         pr = invalid ? -1 : idx;
         if (conf_out) conf_out[row] = c;
         if (pred_out) pred_out[row] = pr;
-        above |= (c > threshold);
+        const bool pass = c > (thr_rows ? thr_rows[row] : threshold);   // false for a NaN threshold
+        above |= pass;
+        s_pass[r] = pass;
         if (!invalid && (c > best_c || (c == best_c && r < best_r))) { best_c = c; best_r = r; }
       }
       s_conf[r] = c;
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
     const int p = s_pred[r];
     if (p == -2) continue;
     const float c = s_conf[r];
-    const bool take = any_above ? (c > threshold) : (r == chosen_row);
+    const bool take = any_above ? (s_pass[r] != 0) : (r == chosen_row);
     if (take) {
       tokens[row0 + r] = p;
       masked[row0 + r] = 0;
@@ -369,7 +373,7 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(commit_decide, dim3(a.n_seq), dim3(kThreads), 0, st, part, nchunk, a.blk_len, a.threshold,
-                     a.fallback_top1, a.tokens, a.masked, a.conf, a.pred, a.n_committed, a.n_masked_left);
+                     a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred, a.n_committed, a.n_masked_left);
   return hipGetLastError();
 }
 

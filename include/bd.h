@@ -174,6 +174,26 @@ bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq
                                int32_t* n_committed, int32_t* n_masked_left,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Confidence commit with a threshold per position (digest, weaknesses,
+ * point 2: the global threshold could give way to local ones that follow the
+ * complexity of each region).
+ *
+ * As bd_confidence_commit, except that row r commits when
+ * conf[r] > thresholds[r]:
+ *   thresholds float32[n_seq*blk_len] (device), read for masked rows only;
+ *        a NaN entry never passes (that row can still be a block's fallback).
+ * The fallback rule is unchanged: a block none of whose masked rows passes
+ * its own threshold commits its most confident masked row (BD_FALLBACK_TOP1).
+ * thresholds == NULL is BD_ERR_NULL; the workspace is the same as for
+ * bd_confidence_commit.
+ * ---------------------------------------------------------------------- */
+bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, const float* thresholds, bd_fallback fallback,
+                                       int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred,
+                                       int32_t* n_committed, int32_t* n_masked_left, void* workspace,
+                                       size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bd_status_string(bd_status s);
 

@@ -20,6 +20,11 @@ Readings where the pages are silent or loose:
 * a row holding NaN or +Inf, or only -Inf, has confidence NaN: it never
   commits and never wins the fallback; -Inf entries alone are legal and add
   nothing to the sum.
+
+A threshold per position (the digest's weaknesses, point 2: local thresholds
+that follow the complexity of each region, in place of one global T) is
+taken as one T_r per row: row r clears it when ``conf_r > T_r``; a NaN T_r is
+never cleared.  The fallback rule is the same as with one threshold.
 """
 from __future__ import annotations
 
@@ -43,8 +48,10 @@ def row_confidence(row: np.ndarray):
 
 
 def confidence_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray,
-                      blk_len: int, threshold: float, fallback: str = FALLBACK_TOP1):
+                      blk_len: int, threshold, fallback: str = FALLBACK_TOP1):
     """One commit step over ``n_seq`` blocks of ``blk_len`` rows each.
+
+    ``threshold`` is one number for every row or an array of one per row.
 
     ``logits [n_seq*blk_len, V]``; ``tokens`` int32 and ``masked`` uint8 (1 =
     still masked) of length ``n_seq*blk_len``.  Rows that are not masked on entry
@@ -64,12 +71,13 @@ def confidence_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray
     for r in range(R):
         if masked[r]:
             conf[r], pred[r] = row_confidence(logits[r])
+    thr = np.broadcast_to(np.asarray(threshold, dtype=np.float64), (R,))
     committed = np.zeros(R, dtype=bool)
     n_committed = np.zeros(n_seq, dtype=np.int32)
     n_left = np.zeros(n_seq, dtype=np.int32)
     for g in range(n_seq):
         rows = range(g * blk_len, (g + 1) * blk_len)
-        chosen = [r for r in rows if masked[r] and not np.isnan(conf[r]) and conf[r] > threshold]
+        chosen = [r for r in rows if masked[r] and not np.isnan(conf[r]) and conf[r] > thr[r]]
         if not chosen and fallback == FALLBACK_TOP1:
             best = None
             for r in rows:

@@ -52,9 +52,11 @@ def grade_commit(ref: dict, gpu: dict, masked_in: np.ndarray, tokens_in: np.ndar
     assert np.array_equal(gpu["tokens"][committed], gpu["pred"][committed])
     assert np.array_equal(gpu["tokens"][m_in & ~committed], tokens_in[m_in & ~committed])
     near_rows, ambiguous = 0, 0
+    thr = np.broadcast_to(np.asarray(T, dtype=np.float64), masked_in.shape)   # one T, or one per row
     for g in range(len(masked_in) // blk_len):
         sl = slice(g * blk_len, (g + 1) * blk_len)
         mg, c, com_g, com_r = m_in[sl], ref["conf"][sl], committed[sl], ref["committed"][sl]
+        T = thr[sl]
         valid = mg & ~np.isnan(c)
         near = valid & (np.abs(c - T) <= band)
         near_rows += int(near.sum())

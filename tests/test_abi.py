@@ -22,7 +22,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L.lib, n), n
     assert set(names) == set(L.EXPORTS)
@@ -117,6 +117,20 @@ def test_commit_validation():
     assert call(fb=7) == L.BD_ERR_VALUE
     assert call(ws=None) == L.BD_ERR_WORKSPACE
     assert call(nb=ws - 16) == L.BD_ERR_WORKSPACE
+
+    def call_rw(**kw):
+        a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, thr=FAKE, fb=1, tok=FAKE, msk=FAKE,
+                 ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_confidence_commit_rowwise(a["lg"], a["stride"], a["n"], a["T"], a["V"], a["dt"], a["thr"],
+                                                  a["fb"], a["tok"], a["msk"], None, None, None, None, a["ws"],
+                                                  a["nb"], None)
+    assert call_rw(thr=None) == L.BD_ERR_NULL
+    assert call_rw(lg=None) == L.BD_ERR_NULL
+    assert call_rw(stride=100) == L.BD_ERR_SHAPE
+    assert call_rw(T=2048) == L.BD_ERR_UNSUPPORTED
+    assert call_rw(fb=7) == L.BD_ERR_VALUE
+    assert call_rw(nb=ws - 16) == L.BD_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors():

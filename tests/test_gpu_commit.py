@@ -22,7 +22,8 @@ def run_case(logits_np, dtype, tokens, masked, blk_len, T, fallback=True, stride
         lg = pad
     tok = torch.from_numpy(tokens.copy()).cuda()
     msk = torch.from_numpy(masked.copy()).cuda()
-    out = bd.bd_confidence_commit(lg, tok, msk, blk_len, T, bd.BD_FALLBACK_TOP1 if fallback else bd.BD_FALLBACK_NONE,
+    thr = torch.from_numpy(np.asarray(T, np.float32)).cuda() if np.ndim(T) else T
+    out = bd.bd_confidence_commit(lg, tok, msk, blk_len, thr, bd.BD_FALLBACK_TOP1 if fallback else bd.BD_FALLBACK_NONE,
                                   vocab=V)
     torch.cuda.synchronize()
     gpu = {"tokens": tok.cpu().numpy(), "masked": msk.cpu().numpy(), "conf": out["conf"].cpu().numpy().astype(np.float64),
@@ -160,3 +161,19 @@ def test_neg_inf_runs():
         for T in (0.3, 0.9):
             near, amb, ref = run_case(arr, dt, tokens, masked, blk, T)
             assert np.isfinite(ref["conf"][[0, 1, 2, 3, 4, 5, 6, 7, 9]]).all()
+
+
+def test_per_row_thresholds():
+    """One threshold per position (bd_confidence_commit_rowwise): random T_r per row, some NaN, some
+    blocks where no row clears its own T (fallback), both dtypes."""
+    banner("commit per-row thresholds")
+    rng = np.random.default_rng(31)
+    for dt, V, n_seq in (("bf16", 151936, 8), ("f32", 5003, 16)):
+        c = W.commit_inputs(n_seq, 32, V, dt, seed=77 + V, masked_frac=0.8, boost=(2.0, 14.0))
+        R = n_seq * 32
+        thr = rng.uniform(0.3, 0.99, R)
+        thr[rng.random(R) < 0.05] = np.nan
+        thr[:32] = 2.0                         # block 0: nothing clears, fallback
+        for fb in (True, False):
+            near, amb, ref = run_case(c["logits"], dt, c["tokens"], c["masked"], 32, thr, fallback=fb)
+            print(f"  {dt} fallback={fb} committed={int(ref['committed'].sum())} near={near} ambiguous={amb}")

@@ -173,3 +173,38 @@ def test_loop_bounds(seed):
     res = DL.decode_loop(n, blk, logits, 0.9)
     assert np.all((res["steps"] >= 1) & (res["steps"] <= blk))
     assert not res["masked"].any() and (res["tokens"] >= 0).all()
+
+
+def test_per_row_thresholds_closed_form():
+    """Per-position thresholds: rows built with a known confidence (one value a, V-1 values 0:
+    conf = 1 / (1 + (V-1) exp(-a))) and each row's own T placed 1e-3 above or below it; the rows
+    that commit are exactly those whose T lies below, whatever the other rows' T."""
+    V, blk, n_seq = 300, 6, 4
+    rng = np.random.default_rng(3)
+    R = n_seq * blk
+    target = rng.uniform(0.2, 0.9, R)
+    gap = np.log((V - 1) * target / (1.0 - target))
+    logits = np.zeros((R, V))
+    ids = rng.integers(0, V, R)
+    logits[np.arange(R), ids] = gap
+    below = rng.random(R) < 0.5
+    below[:blk] = False                       # block 0: nobody clears, fallback takes the top row
+    thr = np.where(below, target - 1e-3, target + 1e-3)
+    thr[blk + 1] = np.nan                     # a NaN threshold is never cleared
+    below[blk + 1] = False
+    masked = np.ones(R, np.uint8)
+    tokens = np.full(R, -1, np.int32)
+    res = C.confidence_commit(logits, tokens, masked, blk, thr)
+    assert np.allclose(res["conf"], target, rtol=0, atol=1e-12)
+    for g in range(n_seq):
+        sl = slice(g * blk, (g + 1) * blk)
+        if below[sl].any():
+            assert np.array_equal(res["committed"][sl], below[sl])
+        else:
+            assert np.flatnonzero(res["committed"][sl]).tolist() == [int(np.argmax(target[sl]))]
+    assert np.array_equal(res["tokens"][res["committed"]], ids[res["committed"]])
+    # a per-row array of one value decides as that single threshold
+    for T in (0.3, 0.6):
+        a = C.confidence_commit(logits, tokens, masked, blk, np.full(R, T))
+        b = C.confidence_commit(logits, tokens, masked, blk, T)
+        assert np.array_equal(a["committed"], b["committed"])
