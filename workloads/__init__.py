@@ -108,6 +108,12 @@ WORKLOADS = {
     # Forward + backward at the second training length (the headline shape).
     "fwdbwd_L16384_bf16": Workload(4, "fwdbwd_L16384_bf16", "bf16", batch=2, seqlen=16384,
                                    n_q_heads=16, n_kv_heads=8, head_dim=128, block_size=32),
+    # The LM head in front of the commit (a "next" row): one block of 32 hidden
+    # states of width 2048 (= 16 heads x 128, the decoder of the 1.7B base named
+    # on the digest page) against a [151936 x 2048] weight; logits never stored.
+    "lmhead_block_bf16": Workload(6, "lmhead_block_bf16", "bf16", batch=1, n_q_heads=16, n_kv_heads=8,
+                                  head_dim=128, block_size=32, vocab=151936, n_seq=1, threshold=0.95,
+                                  boost=(2.0, 14.0)),
     # Batched decode loop: 64 sequences, ragged prefixes U[1024, 16384].
     "decode_loop_bf16": Workload(5, "decode_loop_bf16", "bf16", batch=1, n_q_heads=16, n_kv_heads=8,
                                  head_dim=128, block_size=32, vocab=151936, n_seq=64,
@@ -216,3 +222,35 @@ def commit_inputs(n_seq: int, blk_len: int, vocab: int, dtype: str, seed: int,
             masked[s * blk_len + pos] = 1
     tokens = np.where(masked == 1, -1, rng.integers(0, vocab, size=rows)).astype(np.int32)
     return {"logits": logits, "tokens": tokens, "masked": masked}
+
+
+def lmhead_inputs(n_seq: int, blk_len: int, hidden: int, vocab: int, seed: int,
+                  boost: tuple = (2.0, 14.0), masked_frac: float = 1.0,
+                  rng: Optional[np.random.Generator] = None) -> dict:
+    """Hidden states X [n_seq*blk_len, hidden] ~ N(0,1) and an LM-head weight W [vocab, hidden]
+    ~ N(0, 1/hidden) (so every logit X W^T starts as roughly N(0,1)), both rounded to bf16, plus
+    the token state as in ``commit_inputs``.  Each row r gets a boost b_r ~ U(lo, hi) at one id
+    t_r: W[t_r] += b_r X_r / |X_r|^2 before rounding, which raises logit (r, t_r) by b_r and moves
+    the other rows' logits of id t_r by b_r <X_r', X_r> / |X_r|^2 (about b_r / sqrt(hidden)).
+    The recipe mirrors the boosted synthetic logits of the commit workloads."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    rows = n_seq * blk_len
+    xb = f32_to_bf16_bits(_normal(rng, (rows, hidden)))
+    x = bf16_bits_to_f32(xb)
+    w = _normal(rng, (vocab, hidden), std=float(1.0 / np.sqrt(hidden)))
+    ids = rng.integers(0, vocab, size=rows)
+    b = rng.uniform(boost[0], boost[1], size=rows).astype(np.float32)
+    norm2 = (x.astype(np.float64) ** 2).sum(axis=1)
+    for r in range(rows):
+        w[ids[r]] += (b[r] / norm2[r] * x[r]).astype(np.float32)
+    wb = f32_to_bf16_bits(w)
+    del w
+    if masked_frac >= 1.0:
+        masked = np.ones(rows, np.uint8)
+    else:
+        masked = np.zeros(rows, np.uint8)
+        k = int(round(masked_frac * blk_len))
+        for s in range(n_seq):
+            masked[s * blk_len + rng.permutation(blk_len)[:k]] = 1
+    tokens = np.where(masked == 1, -1, rng.integers(0, vocab, size=rows)).astype(np.int32)
+    return {"hidden": xb, "weight": wb, "boost_ids": ids, "tokens": tokens, "masked": masked}
