@@ -13,7 +13,10 @@ around each forward launch.  The other rows of the metric (decode steps/s,
 commit GB/s, backward TFLOP/s) are reported beside it, together with the
 single-shot decode-step and commit kernels of the 4096-token workload, measured
 over rotating input copies so that the 256 MB Infinity Cache does not serve
-them.  The CPU oracle is timed on a bounded sample on the host.
+them, and the output projection fused with the commit (one block of 32 hidden
+states of width 2048 against a 151936-row weight) beside the unfused path
+(library GEMM to bf16 logits, then the commit).  The CPU oracle is timed on a
+bounded sample on the host.
 
 Prints ONE JSON line.
 """
@@ -152,6 +155,18 @@ def main():
         if have_bwd:
             for _ in range(2):
                 bd.bd_attn_bwd(q, k, v, o, lse, do, blk, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+        hw = W.WORKLOADS["lmhead_block_bf16"]
+        H_lm = hw.n_q_heads * hw.head_dim
+        d_lm = W.lmhead_inputs(1, hw.block_size, H_lm, hw.vocab, hw.seed, boost=hw.boost)
+        x_lm = to_dev(d_lm["hidden"]).view(hw.block_size, H_lm)
+        w_lm = to_dev(d_lm["weight"]).view(hw.vocab, H_lm)
+        del d_lm
+        t_lm = torch.full((hw.block_size,), -1, dtype=torch.int32, device=dev)
+        m_lm = torch.ones(hw.block_size, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            bd.bd_lmhead_commit(x_lm, w_lm, t_lm, m_lm, hw.block_size, 2.0, fallback=bd.BD_FALLBACK_NONE)
+        torch.cuda.synchronize()
+        del x_lm, w_lm
         for i in range(3):
             masked.fill_(1)
             bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
@@ -318,6 +333,43 @@ def main():
     dec1_bytes = (sw.prefix_len + sw.block_size) * Hkv * D * 2 * 2
     com1_bytes = sw.block_size * sw.vocab * 2
 
+    # ------------------ output projection fused with the commit: one block of 32 hidden rows
+    hw = W.WORKLOADS["lmhead_block_bf16"]
+    H_lm = hw.n_q_heads * hw.head_dim
+    d_lm = W.lmhead_inputs(1, hw.block_size, H_lm, hw.vocab, hw.seed, boost=hw.boost)
+    x_lm = to_dev(d_lm["hidden"]).view(hw.block_size, H_lm)
+    w_lm = [to_dev(d_lm["weight"]).view(hw.vocab, H_lm) for _ in range(2)]
+    del d_lm
+    wt_lm = [w.t().contiguous() for w in w_lm]      # [H, V] for the library GEMM of the unfused path
+    tok_lm = torch.full((hw.block_size,), -1, dtype=torch.int32, device=dev)
+    msk_lm = torch.ones(hw.block_size, dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(bd.bd_lmhead_commit_workspace_size(1, hw.block_size, hw.vocab), dtype=torch.uint8,
+                        device=dev)
+    lg_lm = torch.empty((hw.block_size, hw.vocab), dtype=torch.bfloat16, device=dev)
+    cws_lm = torch.empty(bd.bd_confidence_commit_workspace_size(1, hw.block_size, hw.vocab), dtype=torch.uint8,
+                         device=dev)
+
+    # A threshold above 1 without fallback commits nothing, so every call does the same work.
+    def lm_fused(i):
+        bd.bd_lmhead_commit(x_lm, w_lm[i % 2], tok_lm, msk_lm, hw.block_size, 2.0, fallback=bd.BD_FALLBACK_NONE,
+                            want_rows=False, workspace=ws_lm)
+
+    def lm_unfused(i):   # library GEMM to bf16 logits, then the commit kernels
+        torch.mm(x_lm, wt_lm[i % 2], out=lg_lm)
+        bd.bd_confidence_commit(lg_lm, tok_lm, msk_lm, hw.block_size, 2.0, fallback=bd.BD_FALLBACK_NONE,
+                                want_rows=False, workspace=cws_lm)
+
+    lm_us, un_us = [], []
+    for rnd in range(4):
+        t_us = primed([lambda i=i: lm_fused(i) for i in range(8)], n_launch_us=150.0)
+        if rnd:
+            lm_us.extend(t_us)
+        t_us = primed([lambda i=i: lm_unfused(i) for i in range(8)], n_launch_us=150.0)
+        if rnd:
+            un_us.extend(t_us)
+    lm_us, un_us = np.array(lm_us), np.array(un_us)
+    lm_bytes = (hw.vocab + hw.block_size) * H_lm * 2
+
     # --------------------------------------------------------- CPU oracle sample
     cpu = None
     if not args.no_cpu:
@@ -361,6 +413,12 @@ def main():
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(dec1_us, 90)), 2),
                              "GBps": round(dec1_bytes / (np.median(dec1_us) * 1e-6) / 1e9, 1)},
+        "lmhead_commit_32x2048x151936": {"bytes": lm_bytes, "us_median": round(float(np.median(lm_us)), 2),
+                                         "us_p10": round(float(np.percentile(lm_us, 10)), 2),
+                                         "us_p90": round(float(np.percentile(lm_us, 90)), 2),
+                                         "GBps": round(lm_bytes / (np.median(lm_us) * 1e-6) / 1e9, 1),
+                                         "unfused_us_median": round(float(np.median(un_us)), 2),
+                                         "speedup_vs_unfused": round(float(np.median(un_us) / np.median(lm_us)), 3)},
         "commit_32x151936": {"bytes": com1_bytes, "us_median": round(float(np.median(com1_us)), 2),
                              "us_p10": round(float(np.percentile(com1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(com1_us, 90)), 2),

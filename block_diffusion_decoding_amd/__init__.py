@@ -17,7 +17,7 @@ from ._lib import (BD_BF16, BD_F32, BD_FALLBACK_NONE, BD_FALLBACK_TOP1, BdError,
 
 __all__ = [
     "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
-    "bd_confidence_commit_rowwise",
+    "bd_confidence_commit_rowwise", "bd_lmhead_commit", "bd_lmhead_commit_workspace_size",
     "bd_attn_bwd_workspace_size", "bd_attn_decode_workspace_size", "bd_confidence_commit_workspace_size",
     "BdError", "BD_F32", "BD_BF16", "BD_FALLBACK_NONE", "BD_FALLBACK_TOP1", "lib",
 ]
@@ -179,4 +179,42 @@ def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold, fallba
                                       _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb,
                                       _stream(stream))
         check(st, "bd_confidence_commit")
+    return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}
+
+
+def bd_lmhead_commit_workspace_size(n_seq, blk_len, vocab) -> int:
+    return int(lib.bd_lmhead_commit_workspace_size(n_seq, blk_len, vocab))
+
+
+def bd_lmhead_commit(hidden, weight, tokens, masked, blk_len: int, threshold: float,
+                     fallback: int = BD_FALLBACK_TOP1, conf=None, pred=None, n_committed=None, n_masked_left=None,
+                     want_rows: bool = True, workspace=None, stream=None):
+    """Output projection fused with the threshold commit; updates ``tokens``/``masked`` in place.
+
+    hidden bf16 [rows, H] and weight bf16 [vocab, H] (unit stride along H); tokens int32 [rows];
+    masked uint8 [rows].  Returns dict(conf, pred, n_committed, n_masked_left).
+    """
+    rows, H = hidden.shape
+    if rows % blk_len:
+        raise ValueError("hidden rows must be a multiple of blk_len")
+    n_seq = rows // blk_len
+    V = weight.shape[0]
+    for t, name in ((hidden, "hidden"), (weight, "weight")):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor with unit stride along the hidden dimension")
+    if weight.shape[1] != H:
+        raise ValueError("weight must be [vocab, hidden]")
+    _need(tokens, "tokens", (rows,), torch.int32)
+    _need(masked, "masked", (rows,), torch.uint8)
+    dev = hidden.device
+    if want_rows:
+        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
+        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
+    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
+    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    ws, nb = _workspace(bd_lmhead_commit_workspace_size(n_seq, blk_len, V), dev, workspace)
+    st = lib.bd_lmhead_commit(_ptr(hidden), hidden.stride(0), _ptr(weight), weight.stride(0), n_seq, blk_len, H, V,
+                              float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred),
+                              _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
+    check(st, "bd_lmhead_commit")
     return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}

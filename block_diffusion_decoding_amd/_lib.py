@@ -37,6 +37,8 @@ _SIGS = {
     "bd_confidence_commit_workspace_size": (_sz, [_i, _i, _i]),
     "bd_confidence_commit": (_i, [_p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "bd_confidence_commit_rowwise": (_i, [_p, _i64, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "bd_lmhead_commit_workspace_size": (_sz, [_i, _i, _i]),
+    "bd_lmhead_commit": (_i, [_p, _i64, _p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }
 
 EXPORTS = tuple(_SIGS)

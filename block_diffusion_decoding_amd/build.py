@@ -26,7 +26,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 
-SOURCES = ["bd_api.cpp", "commit.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip"]
+SOURCES = ["bd_api.cpp", "commit.hip", "lmhead.hip", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip",
+           "attn_f32.hip"]
 # The decode kernel keeps its matrix accumulators in ordinary VGPRs (otherwise
 # the compiler parks them in AGPRs and copies them back and forth every tile).
 PER_FILE = {"attn_decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],

@@ -189,4 +189,37 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
                        masked, conf, pred, n_committed, n_masked_left, workspace, ws_bytes, stream);
 }
 
+size_t bd_lmhead_commit_workspace_size(int n_seq, int blk_len, int vocab) {
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  return bd::lmhead_workspace_bytes(n_seq, blk_len);
+}
+
+bd_status bd_lmhead_commit(const void* hidden, int64_t hidden_stride, const void* weight, int64_t weight_stride,
+                           int n_seq, int blk_len, int hidden_dim, int vocab, float threshold, bd_fallback fallback,
+                           int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
+                           int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!hidden || !weight || !tokens || !masked) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || hidden_dim <= 0) return BD_ERR_SHAPE;
+  if (hidden_stride < hidden_dim || weight_stride < hidden_dim) return BD_ERR_SHAPE;
+  if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
+  if (hidden_dim % 64 != 0 || hidden_dim > bd::lmhead_max_hidden()) return BD_ERR_UNSUPPORTED;
+  if (!aligned16(hidden) || !aligned16(weight) || hidden_stride % 8 != 0 || weight_stride % 8 != 0)
+    return BD_ERR_ALIGNMENT;
+  if (std::isnan(threshold)) return BD_ERR_VALUE;
+  if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
+  if ((long long)n_seq * blk_len > kMaxGrid / 256) return BD_ERR_SHAPE;
+  const size_t need = bd::lmhead_workspace_bytes(n_seq, blk_len);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  bd::LmHeadArgs a;
+  a.hidden = hidden;
+  a.hidden_stride = hidden_stride;
+  a.weight = weight;
+  a.weight_stride = weight_stride;
+  a.hidden_dim = hidden_dim;
+  a.commit = bd::CommitArgs{nullptr, 0, n_seq, blk_len, vocab, 1, threshold, nullptr,
+                            fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left,
+                            workspace};
+  return hip_status(bd::launch_lmhead_commit(a, stream));
+}
+
 }  // extern "C"

@@ -62,7 +62,22 @@ struct CommitArgs {
 int commit_chunks_per_row(long long rows, int vocab);
 size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+// The decide step alone, on nchunk partials per row at `part` ([row][chunk]).
+hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st);
 
 constexpr int kCommitMaxBlock = 1024;  // largest blk_len the commit kernel takes
+
+// ---- output projection fused with the confidence reduce ---------------------
+struct LmHeadArgs {
+  const void* hidden;   // [rows, hidden_dim] bf16
+  int64_t hidden_stride;
+  const void* weight;   // [vocab, hidden_dim] bf16
+  int64_t weight_stride;
+  int hidden_dim;
+  CommitArgs commit;    // logits unused; vocab, state, outputs and workspace as for the commit
+};
+int lmhead_max_hidden();
+size_t lmhead_workspace_bytes(int n_seq, int blk_len);
+hipError_t launch_lmhead_commit(const LmHeadArgs& a, hipStream_t st);
 
 }  // namespace bd

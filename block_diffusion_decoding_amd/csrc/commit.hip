@@ -18,6 +18,7 @@
 // The HBM traffic is the logits of the masked rows plus a few bytes per row.
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
+#include "commit_common.hpp"
 
 #include <algorithm>
 
@@ -34,27 +35,7 @@ constexpr int kStep = 2048;          // vocabulary entries per workgroup and loa
 constexpr int kTargetWGs = BD_COMMIT_TARGET_WGS;   // workgroups the chunking aims for
 constexpr int kMinChunk = 4096;      // fewest vocabulary entries per chunk
 constexpr int kDecideLanes = 8;      // threads merging one row's partials
-
-struct Partial {
-  float m;    // max of the chunk (-inf if the chunk holds only -inf)
-  float s;    // sum over the chunk of exp(x - m)
-  int idx;    // lowest id reaching m
-  int bad;    // chunk holds a NaN or +Inf
-};
-
-// Merge (m2, s2, i2) into (m, s, i).  Sums are kept relative to their max.
-__device__ __forceinline__ void merge_state(float& m, float& s, int& idx, float m2, float s2, int i2) {
-  if (m2 > m) {
-    s = s * exp2_fast((m - m2) * kLog2e) + s2;
-    m = m2;
-    idx = i2;
-  } else if (m2 == m) {
-    s += s2;
-    idx = min(idx, i2);
-  } else {
-    s += s2 * exp2_fast((m2 - m) * kLog2e);
-  }
-}
+constexpr int kMergeBatch = 8;       // partial loads in flight per merging thread
 
 template <typename T> struct Vec;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -77,54 +58,6 @@ template <> struct Vec<float> {
   __device__ static void unpack(const Raw& f, float* x) { x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w; }
   __device__ static float scalar(const float* p) { return *p; }
 };
-
-// Running per-thread state over the ids it has seen (in increasing order):
-// m = max, idx = lowest id reaching m, s = sum exp(x - m), bad = a NaN was
-// summed before a later rescale could hide it.  A NaN element makes s NaN; a
-// +Inf element makes m +Inf and s NaN; an element -Inf contributes 0.
-struct RowState {
-  float m = kNegInf, s = 0.f;
-  float mb = 0.f;   // m * log2(e) once m is finite; 0 while m = -inf (then every exponent is -inf)
-  int idx = 0x7fffffff, bad = 0;
-};
-
-// A new maximum mx > st.m at id: rescale the sum (a NaN summed so far is
-// recorded first, since the rescale by 0 could hide it).
-__device__ __forceinline__ void raise_max(RowState& st, float mx, int id) {
-  st.bad |= st.s != st.s;
-  st.s = st.m == kNegInf ? 0.f : st.s * exp2_fast((st.m - mx) * kLog2e);
-  st.m = mx;
-  st.mb = mx * kLog2e;
-  st.idx = id;
-}
-
-// Fold the N values starting at vocabulary id `base` (all valid).
-template <int N>
-__device__ __forceinline__ void fold_vec(const float* x, int base, RowState& st) {
-  float vmax = x[0];
-#pragma unroll
-  for (int j = 1; j < N; ++j) vmax = fmaxf(vmax, x[j]);
-  if (vmax > st.m) {   // new maximum (rare after the first few vectors)
-    int j0 = N - 1;
-#pragma unroll
-    for (int j = N - 2; j >= 0; --j) j0 = x[j] == vmax ? j : j0;
-    raise_max(st, vmax, base + j0);
-  }
-  float e[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) e[j] = exp2_fast(__builtin_fmaf(x[j], kLog2e, -st.mb));
-#pragma unroll
-  for (int w = 1; w < N; w *= 2)
-#pragma unroll
-    for (int j = 0; j < N; j += 2 * w) e[j] += e[j + w];
-  st.s += e[0];
-}
-
-// A single value (ragged tail / unaligned rows).
-__device__ __forceinline__ void fold_one(float x, int id, RowState& st) {
-  if (x > st.m) raise_max(st, x, id);
-  st.s += exp2_fast(__builtin_fmaf(x, kLog2e, -st.mb));
-}
 
 template <typename T, bool kVector>
 __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ logits, int64_t row_stride,
@@ -220,7 +153,9 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restrict__ part, int nchunk,
+// kLanes threads per row merge its partials; kThr threads per workgroup.
+template <int kLanes, int kThr>
+__global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict__ part, int nchunk,
                                                           int blk_len, float threshold,
                                                           const float* __restrict__ thr_rows, int fallback_top1,
                                                           int32_t* __restrict__ tokens,
@@ -232,35 +167,43 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
   __shared__ float s_conf[kCommitMaxBlock];
   __shared__ int s_pred[kCommitMaxBlock];
   __shared__ unsigned char s_pass[kCommitMaxBlock];
-  __shared__ float s_best_c[kThreads / 64];
-  __shared__ int s_best_r[kThreads / 64];
+  __shared__ float s_best_c[kThr / 64];
+  __shared__ int s_best_r[kThr / 64];
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t row0 = (int64_t)g * blk_len;
 
-  // kDecideLanes threads per row merge its chunk partials (strided), then
+  // kLanes threads per row merge its chunk partials (strided), then
   // combine across the group; the group's first thread finishes the row.
   int above = 0;
   float best_c = kNegInf;
   int best_r = 0x7fffffff;
-  const int sub = tid % kDecideLanes;
-  for (int r0 = 0; r0 < blk_len; r0 += kThreads / kDecideLanes) {
-    const int r = r0 + tid / kDecideLanes;
+  const int sub = tid % kLanes;
+  for (int r0 = 0; r0 < blk_len; r0 += kThr / kLanes) {
+    const int r = r0 + tid / kLanes;
     const bool in = r < blk_len;
     const int64_t row = row0 + (in ? r : 0);
     const bool msk = in && masked[row];
     float m = kNegInf, s = 0.f;
     int idx = 0x7fffffff, bad = 0;
     if (msk) {
+      // partials in batches of kMergeBatch loads per round trip to memory
       const Partial* pp = part + row * nchunk;
-      for (int k = sub; k < nchunk; k += kDecideLanes) {
-        const Partial q = pp[k];
-        if (!bad && !q.bad) merge_state(m, s, idx, q.m, q.s, q.idx);
-        bad |= q.bad;
+      for (int kb = sub; kb < nchunk; kb += kMergeBatch * kLanes) {
+        Partial q[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+          if (kb + i * kLanes < nchunk) q[i] = pp[kb + i * kLanes];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+          if (kb + i * kLanes < nchunk) {
+            if (!bad && !q[i].bad) merge_state(m, s, idx, q[i].m, q[i].s, q[i].idx);
+            bad |= q[i].bad;
+          }
       }
     }
 #pragma unroll
-    for (int off = 1; off < kDecideLanes; off <<= 1) {
+    for (int off = 1; off < kLanes; off <<= 1) {
       float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
       int i2 = __shfl_xor(idx, off, 64), b2 = __shfl_xor(bad, off, 64);
       if (!bad && !b2) merge_state(m, s, idx, m2, s2, i2);
@@ -298,14 +241,14 @@ __global__ __launch_bounds__(kThreads) void commit_decide(const Partial* __restr
     __syncthreads();
     float bc = s_best_c[0];
     int br = s_best_r[0];
-    for (int w = 1; w < kThreads / 64; ++w) {
+    for (int w = 1; w < kThr / 64; ++w) {
       if (s_best_c[w] > bc || (s_best_c[w] == bc && s_best_r[w] < br)) { bc = s_best_c[w]; br = s_best_r[w]; }
     }
     chosen_row = (br < blk_len) ? br : -1;
   }
 
   int committed = 0, left = 0;
-  for (int r = tid; r < blk_len; r += kThreads) {
+  for (int r = tid; r < blk_len; r += kThr) {
     const int p = s_pred[r];
     if (p == -2) continue;
     const float c = s_conf[r];
@@ -372,8 +315,20 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_decide, dim3(a.n_seq), dim3(kThreads), 0, st, part, nchunk, a.blk_len, a.threshold,
-                     a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred, a.n_committed, a.n_masked_left);
+  return launch_commit_decide(part, nchunk, a, st);
+}
+
+hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st) {
+  // Rows with many partials (the fused projection: one per workgroup) get 32 threads each.
+  const Partial* pp = reinterpret_cast<const Partial*>(part);
+  if (nchunk >= 64)
+    hipLaunchKernelGGL((commit_decide<32, 1024>), dim3(a.n_seq), dim3(1024), 0, st, pp, nchunk, a.blk_len,
+                       a.threshold, a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred,
+                       a.n_committed, a.n_masked_left);
+  else
+    hipLaunchKernelGGL((commit_decide<kDecideLanes, kThreads>), dim3(a.n_seq), dim3(kThreads), 0, st, pp, nchunk,
+                       a.blk_len, a.threshold, a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred,
+                       a.n_committed, a.n_masked_left);
   return hipGetLastError();
 }
 

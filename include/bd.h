@@ -194,6 +194,37 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
                                        int32_t* n_committed, int32_t* n_masked_left, void* workspace,
                                        size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Output projection fused with the confidence commit.  The commit acts on the
+ * prediction of each masked position (digest, method step 4), the decoder's
+ * distribution over the shared vocabulary (method step 1): the softmax of the
+ * logits that the output projection makes from the last hidden states.  Here
+ * the logits are never stored:
+ *
+ *   logits[r][v] = sum_k hidden[r][k] * weight[v][k]   (fp32 accumulation)
+ *
+ * and the rows then follow bd_confidence_commit exactly (conf, pred, the
+ * threshold rule, the fallback, the state update), with conf and pred taken
+ * from the fp32 logits.
+ *
+ *   hidden [n_seq*blk_len, hidden_dim] bf16, row r at hidden + r*hidden_stride
+ *   weight [vocab, hidden_dim] bf16, row v at weight + v*weight_stride
+ *        (both base pointers 16-byte aligned, strides multiples of 8 elements:
+ *        BD_ERR_ALIGNMENT otherwise)
+ *   hidden_dim a multiple of 64, at most 2048 (BD_ERR_UNSUPPORTED otherwise)
+ *   threshold, fallback, tokens, masked, conf, pred, n_committed,
+ *        n_masked_left: as bd_confidence_commit
+ *   workspace of bd_lmhead_commit_workspace_size() bytes (per-row partial
+ *        states); contents on entry are ignored.
+ * Each group of 32 rows that holds a masked row reads the whole weight once
+ * (one block of 32 rows: the weight is streamed from HBM once).
+ * ---------------------------------------------------------------------- */
+size_t bd_lmhead_commit_workspace_size(int n_seq, int blk_len, int vocab);
+bd_status bd_lmhead_commit(const void* hidden, int64_t hidden_stride, const void* weight, int64_t weight_stride,
+                           int n_seq, int blk_len, int hidden_dim, int vocab, float threshold, bd_fallback fallback,
+                           int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
+                           int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bd_status_string(bd_status s);
 

@@ -22,7 +22,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L.lib, n), n
     assert set(names) == set(L.EXPORTS)
@@ -131,6 +131,30 @@ def test_commit_validation():
     assert call_rw(T=2048) == L.BD_ERR_UNSUPPORTED
     assert call_rw(fb=7) == L.BD_ERR_VALUE
     assert call_rw(nb=ws - 16) == L.BD_ERR_WORKSPACE
+
+
+def test_lmhead_validation():
+    ws = L.lib.bd_lmhead_commit_workspace_size(1, 32, 151936)
+    assert ws == 32 * 256 * 16      # one 16-byte partial per (row, workgroup)
+
+    def call(**kw):
+        a = dict(x=FAKE, xs=2048, w=FAKE, wsd=2048, n=1, T=32, H=2048, V=151936, thr=0.95, fb=1, tok=FAKE,
+                 msk=FAKE, ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_lmhead_commit(a["x"], a["xs"], a["w"], a["wsd"], a["n"], a["T"], a["H"], a["V"], a["thr"],
+                                      a["fb"], a["tok"], a["msk"], None, None, None, None, a["ws"], a["nb"], None)
+    assert call(x=None) == L.BD_ERR_NULL
+    assert call(w=None) == L.BD_ERR_NULL
+    assert call(msk=None) == L.BD_ERR_NULL
+    assert call(V=0) == L.BD_ERR_SHAPE
+    assert call(xs=100) == L.BD_ERR_SHAPE
+    assert call(H=2056, xs=2056, wsd=2056) == L.BD_ERR_UNSUPPORTED      # more than 2048
+    assert call(H=96, xs=96, wsd=96) == L.BD_ERR_UNSUPPORTED            # not a multiple of 64
+    assert call(x=MIS) == L.BD_ERR_ALIGNMENT
+    assert call(wsd=2052) == L.BD_ERR_ALIGNMENT
+    assert call(thr=math.nan) == L.BD_ERR_VALUE
+    assert call(fb=3) == L.BD_ERR_VALUE
+    assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors():
