@@ -33,10 +33,12 @@ Modules:
 * :mod:`oracle.decode_loop` -- the per-block denoising loop as a state machine.
 * :mod:`oracle.lmhead` -- the output projection feeding the commit (logits =
   hidden x weight^T), for the fused projection + confidence kernel.
+* :mod:`oracle.sampling` -- the commit with sampled predictions (temperature,
+  inverse-CDF sampling from a counter-based generator).
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than
 itself (library routines in special cases, closed forms, invariants, brute
 force and finite differences).  No function here is "parity unpinned".
 """
 
-from . import attention, commit, decode_loop, lmhead  # noqa: F401
+from . import attention, commit, decode_loop, lmhead, sampling  # noqa: F401

@@ -62,15 +62,25 @@ def confidence_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray
     """
     logits = np.asarray(logits)
     R = logits.shape[0]
-    assert R % blk_len == 0
-    n_seq = R // blk_len
-    tokens = np.array(tokens, dtype=np.int32, copy=True)
-    masked = np.array(masked, dtype=np.uint8, copy=True)
     conf = np.full(R, np.nan)
     pred = np.full(R, -1, dtype=np.int32)
     for r in range(R):
         if masked[r]:
             conf[r], pred[r] = row_confidence(logits[r])
+    return decide(conf, pred, tokens, masked, blk_len, threshold, fallback)
+
+
+def decide(conf: np.ndarray, pred: np.ndarray, tokens: np.ndarray, masked: np.ndarray,
+           blk_len: int, threshold, fallback: str = FALLBACK_TOP1):
+    """The threshold rule, the fallback and the state update, given each masked row's confidence
+    and predicted id (NaN / -1 for invalid rows)."""
+    R = len(conf)
+    assert R % blk_len == 0
+    n_seq = R // blk_len
+    tokens = np.array(tokens, dtype=np.int32, copy=True)
+    masked = np.array(masked, dtype=np.uint8, copy=True)
+    conf = np.asarray(conf, dtype=np.float64)
+    pred = np.asarray(pred, dtype=np.int32)
     thr = np.broadcast_to(np.asarray(threshold, dtype=np.float64), (R,))
     committed = np.zeros(R, dtype=bool)
     n_committed = np.zeros(n_seq, dtype=np.int32)
@@ -91,5 +101,5 @@ def confidence_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray
             masked[r] = 0
         n_committed[g] = len(chosen)
         n_left[g] = int(masked[g * blk_len:(g + 1) * blk_len].sum())
-    return {"tokens": tokens, "masked": masked, "conf": conf, "pred": pred,
+    return {"tokens": tokens, "masked": masked, "conf": conf.copy(), "pred": pred.copy(),
             "n_committed": n_committed, "n_masked_left": n_left, "committed": committed}
