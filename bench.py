@@ -295,6 +295,21 @@ def main():
             rw_us.extend(t_us)
     rw_bytes = n_rows * V * 2
 
+    # sampled predictions at temperature 1 (bd_confidence_commit_sampled) on the all-masked first step
+    sm_ws = torch.empty(bd.bd_confidence_commit_sampled_workspace_size(lw.n_seq, lw.block_size, V), dtype=torch.uint8,
+                        device=dev)
+    sm_us = []
+    for rnd in range(4):
+        for m in msk_rw:
+            m.fill_(1)
+        t_us = primed([lambda i=i: bd.bd_confidence_commit_sampled(logit_pool[i], tokens, msk_rw[i], lw.block_size,
+                                                                   T_step, temperature=1.0, seed=lw.seed, step=rnd,
+                                                                   conf=conf, pred=pred, n_committed=ncom,
+                                                                   n_masked_left=nleft, workspace=sm_ws)
+                       for i in range(n_pool)])
+        if rnd:
+            sm_us.extend(t_us)
+
     # ------------------------------- single-shot decode step / commit, 4096 prefix
     sw = W.WORKLOADS["decode_step_bf16"]
     n_copies_kv, n_copies_lg = 40, 64
@@ -408,6 +423,7 @@ def main():
                         "commit_GBps_first_step": round(com_gbs_loop[0], 1),
                         "commit_GBps_median": round(float(np.median(com_gbs_loop)), 1),
                         "commit_rowwise_GBps_first_step": round(rw_bytes / (np.median(rw_us) * 1e-6) / 1e9, 1),
+                        "commit_sampled_GBps_first_step": round(rw_bytes / (np.median(sm_us) * 1e-6) / 1e9, 1),
                         "by_threshold": loops},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),

@@ -18,6 +18,7 @@ from ._lib import (BD_BF16, BD_F32, BD_FALLBACK_NONE, BD_FALLBACK_TOP1, BdError,
 __all__ = [
     "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
     "bd_confidence_commit_rowwise", "bd_lmhead_commit", "bd_lmhead_commit_workspace_size",
+    "bd_confidence_commit_sampled", "bd_confidence_commit_sampled_workspace_size",
     "bd_attn_bwd_workspace_size", "bd_attn_decode_workspace_size", "bd_confidence_commit_workspace_size",
     "BdError", "BD_F32", "BD_BF16", "BD_FALLBACK_NONE", "BD_FALLBACK_TOP1", "lib",
 ]
@@ -217,4 +218,38 @@ def bd_lmhead_commit(hidden, weight, tokens, masked, blk_len: int, threshold: fl
                               float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred),
                               _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
     check(st, "bd_lmhead_commit")
+    return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}
+
+
+def bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, vocab) -> int:
+    return int(lib.bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, vocab))
+
+
+def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold: float, temperature: float = 1.0,
+                                 seed: int = 0, step: int = 0, fallback: int = BD_FALLBACK_TOP1,
+                                 vocab: Optional[int] = None, conf=None, pred=None, n_committed=None,
+                                 n_masked_left=None, want_rows: bool = True, workspace=None, stream=None):
+    """Threshold commit with sampled predictions (temperature, Philox4x32-10 keyed by seed/row/step);
+    updates ``tokens``/``masked`` in place.  Returns dict(conf, pred, n_committed, n_masked_left)."""
+    rows = logits.shape[0]
+    if rows % blk_len:
+        raise ValueError("logits rows must be a multiple of blk_len")
+    n_seq = rows // blk_len
+    V = logits.shape[1] if vocab is None else int(vocab)
+    if not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
+    _need(tokens, "tokens", (rows,), torch.int32)
+    _need(masked, "masked", (rows,), torch.uint8)
+    dev = logits.device
+    if want_rows:
+        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
+        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
+    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
+    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    ws, nb = _workspace(bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, V), dev, workspace)
+    st = lib.bd_confidence_commit_sampled(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
+                                          float(temperature), int(seed), int(step), float(threshold), int(fallback),
+                                          _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred), _ptr(n_committed),
+                                          _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
+    check(st, "bd_confidence_commit_sampled")
     return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}

@@ -23,6 +23,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 _p, _i, _f, _sz, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
+_u64 = ctypes.c_uint64
 
 _SIGS = {
     "bd_status_string": (ctypes.c_char_p, [_i]),
@@ -37,6 +38,9 @@ _SIGS = {
     "bd_confidence_commit_workspace_size": (_sz, [_i, _i, _i]),
     "bd_confidence_commit": (_i, [_p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "bd_confidence_commit_rowwise": (_i, [_p, _i64, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "bd_confidence_commit_sampled_workspace_size": (_sz, [_i, _i, _i]),
+    "bd_confidence_commit_sampled": (_i, [_p, _i64, _i, _i, _i, _i, _f, _u64, _u64, _f, _i, _p, _p, _p, _p, _p, _p,
+                                         _p, _sz, _p]),
     "bd_lmhead_commit_workspace_size": (_sz, [_i, _i, _i]),
     "bd_lmhead_commit": (_i, [_p, _i64, _p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }

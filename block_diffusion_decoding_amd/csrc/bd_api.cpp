@@ -189,6 +189,32 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
                        masked, conf, pred, n_committed, n_masked_left, workspace, ws_bytes, stream);
 }
 
+size_t bd_confidence_commit_sampled_workspace_size(int n_seq, int blk_len, int vocab) {
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  return bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
+}
+
+bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step,
+                                       float threshold, bd_fallback fallback, int32_t* tokens, uint8_t* masked,
+                                       float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
+                                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !tokens || !masked) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || row_stride < vocab) return BD_ERR_SHAPE;
+  if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
+  if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
+  if (std::isnan(threshold)) return BD_ERR_VALUE;
+  if (!(temperature > 0.f) || std::isinf(temperature)) return BD_ERR_VALUE;
+  if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
+  const long long rows = (long long)n_seq * blk_len;
+  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
+  const size_t need = bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, nullptr,
+                   fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
+  return hip_status(bd::launch_commit_sampled(a, temperature, seed, step, stream));
+}
+
 size_t bd_lmhead_commit_workspace_size(int n_seq, int blk_len, int vocab) {
   if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
   return bd::lmhead_workspace_bytes(n_seq, blk_len);

@@ -62,6 +62,10 @@ struct CommitArgs {
 int commit_chunks_per_row(long long rows, int vocab);
 size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+// Sampled predictions at `temperature` (Philox4x32-10 keyed by seed, row, step).
+size_t commit_sampled_workspace_bytes(int n_seq, int blk_len, int vocab);
+hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
+                                 hipStream_t st);
 // The decide step alone, on nchunk partials per row at `part` ([row][chunk]).
 hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st);
 

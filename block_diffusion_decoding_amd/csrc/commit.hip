@@ -33,6 +33,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kStep = 2048;          // vocabulary entries per workgroup and load step (bf16)
 constexpr int kTargetWGs = BD_COMMIT_TARGET_WGS;   // workgroups the chunking aims for
+// Sampling rescans one chunk per row: finer chunks keep that rescan short.
+constexpr int kSampleTargetWGs = 4 * BD_COMMIT_TARGET_WGS;
 constexpr int kMinChunk = 4096;      // fewest vocabulary entries per chunk
 constexpr int kDecideLanes = 8;      // threads merging one row's partials
 constexpr int kMergeBatch = 8;       // partial loads in flight per merging thread
@@ -63,7 +65,7 @@ template <typename T, bool kVector>
 __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ logits, int64_t row_stride,
                                                           int vocab, int nchunk, int chunk_len,
                                                           const uint8_t* __restrict__ masked,
-                                                          Partial* __restrict__ part) {
+                                                          Partial* __restrict__ part, float c) {
   const int row = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - row * nchunk;
   if (!masked[row]) return;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
     auto fold = [&](const Raw& r, int v) __attribute__((always_inline)) {
       float x[N];
       Vec<T>::unpack(r, x);
-      fold_vec<N>(x, c0 + (v * kThreads + tid) * N, st);
+      fold_vec<N>(x, c0 + (v * kThreads + tid) * N, st, c);
     };
     Raw buf[kA];
     if (nv >= 2 * kA) {
@@ -121,9 +123,9 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
           if (h * kA + u < nv) fold(buf[u], h * kA + u);
       }
     }
-    for (int q = full + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st);
+    for (int q = full + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st, c);
   } else {
-    for (int q = c0 + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st);
+    for (int q = c0 + tid; q < c1; q += kThreads) fold_one(Vec<T>::scalar(base + q), q, st, c);
   }
   st.bad |= (st.s != st.s) | (st.m == __builtin_huge_valf());
 
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
   for (int off = 32; off >= 1; off >>= 1) {
     float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
     int i2 = __shfl_xor(idx, off, 64), b2 = __shfl_xor(bad, off, 64);
-    if (!bad && !b2) merge_state(m, s, idx, m2, s2, i2);
+    if (!bad && !b2) merge_state(m, s, idx, m2, s2, i2, c);
     bad |= b2;
   }
   __shared__ Partial red[kThreads / 64];
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
     Partial r = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) {
-      if (!r.bad && !red[w].bad) merge_state(r.m, r.s, r.idx, red[w].m, red[w].s, red[w].idx);
+      if (!r.bad && !red[w].bad) merge_state(r.m, r.s, r.idx, red[w].m, red[w].s, red[w].idx, c);
       r.bad |= red[w].bad;
     }
     part[(int64_t)row * nchunk + chunk] = r;
@@ -154,8 +156,12 @@ __global__ __launch_bounds__(kThreads) void commit_reduce(const T* __restrict__ 
 }
 
 // kLanes threads per row merge its partials; kThr threads per workgroup.
+// With row_conf / row_pred set, each masked row's (conf, id) is taken from
+// them (a prediction made elsewhere, e.g. sampled) and no partial is read.
 template <int kLanes, int kThr>
 __global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict__ part, int nchunk,
+                                                          const float* __restrict__ row_conf,
+                                                          const int32_t* __restrict__ row_pred,
                                                           int blk_len, float threshold,
                                                           const float* __restrict__ thr_rows, int fallback_top1,
                                                           int32_t* __restrict__ tokens,
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict_
     const bool msk = in && masked[row];
     float m = kNegInf, s = 0.f;
     int idx = 0x7fffffff, bad = 0;
-    if (msk) {
+    if (msk && !row_conf) {
       // partials in batches of kMergeBatch loads per round trip to memory
       const Partial* pp = part + row * nchunk;
       for (int kb = sub; kb < nchunk; kb += kMergeBatch * kLanes) {
@@ -213,9 +219,16 @@ __global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict_
       float c = __builtin_nanf("");
       int pr = -2;  // -2: not masked on entry
       if (msk) {
-        const bool invalid = bad || (m == kNegInf);
-        c = invalid ? __builtin_nanf("") : 1.0f / s;
-        pr = invalid ? -1 : idx;
+        bool invalid;
+        if (row_conf) {
+          pr = row_pred[row];
+          invalid = pr < 0;
+          c = invalid ? __builtin_nanf("") : row_conf[row];
+        } else {
+          invalid = bad || (m == kNegInf);
+          c = invalid ? __builtin_nanf("") : 1.0f / s;
+          pr = invalid ? -1 : idx;
+        }
         if (conf_out) conf_out[row] = c;
         if (pred_out) pred_out[row] = pr;
         const bool pass = c > (thr_rows ? thr_rows[row] : threshold);   // false for a NaN threshold
@@ -276,15 +289,281 @@ __global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict_
 // Vocabulary entries per chunk for rows x vocab logits: about kTargetWGs
 // workgroups in all, chunks of at least kMinChunk entries, a multiple of
 // kStep (so that every chunk but a row's last starts and ends on whole steps).
-int commit_chunk_len(long long rows, int vocab) {
-  const long long want = std::max<long long>(1, (kTargetWGs + rows - 1) / rows);
+int commit_chunk_len(long long rows, int vocab, long long target_wgs = kTargetWGs) {
+  const long long want = std::max<long long>(1, (target_wgs + rows - 1) / rows);
   const long long most = std::max<long long>(1, (vocab + kMinChunk - 1) / kMinChunk);
   const long long nchunk = std::min(want, most);
   const long long len = (vocab + nchunk - 1) / nchunk;
   return (int)(((len + kStep - 1) / kStep) * kStep);
 }
 
+// ---- sampled predictions ----------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of the two 32 x 32 -> 64-bit products of
+// counter words 0 and 2, the key bumped by the Weyl constants between rounds;
+// word 0 of the output block.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+
+// One workgroup per masked row: merge the row's chunk partials (max M, sum S of
+// 2^((x - M) c)), draw u for (seed, row, step), find the chunk in which the
+// running sum (chunks in id order) passes u S, rescan that chunk in id order
+// (each thread a contiguous slice, a workgroup scan of the slice sums) and take
+// the first id whose running sum passes u S.  conf = 2^((x_id - M) c) / S.
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kThreads) void sample_locate(const T* __restrict__ logits, int64_t row_stride,
+                                                          int vocab, int nchunk, int chunk_len,
+                                                          const uint8_t* __restrict__ masked,
+                                                          const Partial* __restrict__ part, float c, uint32_t seed_lo,
+                                                          uint32_t seed_hi, uint32_t step_lo, uint32_t step_hi,
+                                                          float* __restrict__ row_conf,
+                                                          int32_t* __restrict__ row_pred) {
+  constexpr int N = Vec<T>::N;
+  const int row = blockIdx.x;
+  if (!masked[row]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_M, s_S, s_res;
+  __shared__ int s_chunk, s_ok;
+  __shared__ float s_wsum[kThreads / 64];
+  __shared__ int s_found, s_last, s_idx;
+
+  if (wave == 0) {
+    // total over the chunks, then the chunk holding the target (chunks of 64 at a time)
+    Partial tot{kNegInf, 0.f, 0x7fffffff, 0};
+    for (int k0 = 0; k0 < nchunk; k0 += 64) {
+      Partial q{kNegInf, 0.f, 0x7fffffff, 0};
+      if (k0 + lane < nchunk) q = part[(int64_t)row * nchunk + k0 + lane];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        Partial o{__shfl_xor(q.m, off, 64), __shfl_xor(q.s, off, 64), __shfl_xor(q.idx, off, 64),
+                  __shfl_xor(q.bad, off, 64)};
+        merge_partial(q, o, c);
+      }
+      merge_partial(tot, q, c);
+    }
+    const bool ok = !tot.bad && tot.m != kNegInf;
+    // the last chunk holding a finite value (a target past the end, from rounding, takes its last id)
+    int last_chunk = 0;
+    for (int k0 = 0; k0 < nchunk; k0 += 64) {
+      const bool fin = k0 + lane < nchunk && part[(int64_t)row * nchunk + k0 + lane].m != kNegInf;
+      const unsigned long long b = __builtin_amdgcn_ballot_w64(fin);
+      if (b) last_chunk = k0 + 63 - __builtin_clzll(b);
+    }
+    const uint32_t w = philox_word0((uint32_t)row, step_lo, step_hi, 0u, seed_lo, seed_hi);
+    const float u = (float)(((double)w + 0.5) * (1.0 / 4294967296.0));
+    const float target = u * tot.s;
+    int chunk = last_chunk;
+    float before = 0.f;
+    bool found = false;
+    if (ok) {
+      for (int k0 = 0; k0 < nchunk && !found; k0 += 64) {
+        float v = 0.f;
+        if (k0 + lane < nchunk) {
+          const Partial q = part[(int64_t)row * nchunk + k0 + lane];
+          v = q.m == kNegInf ? 0.f : q.s * exp2_fast((q.m - tot.m) * c);
+        }
+        float incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(k0 + lane < nchunk && before + incl > target);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          chunk = k0 + l;
+          before += __shfl(incl, l, 64) - __shfl(v, l, 64);
+          found = true;
+        } else {
+          before += __shfl(incl, 63, 64);
+        }
+      }
+    }
+    if (lane == 0) {
+      s_ok = ok;
+      s_M = tot.m;
+      s_S = tot.s;
+      s_chunk = chunk;
+      s_res = found ? target - before : 3.4e38f;   // past the end: the last id of positive weight
+      s_found = 0x7fffffff;
+      s_last = -1;
+      s_idx = tot.idx;
+    }
+  }
+  __syncthreads();
+  if (!s_ok) {
+    if (tid == 0) {
+      row_conf[row] = __builtin_nanf("");
+      row_pred[row] = -1;
+    }
+    return;
+  }
+  const float M = s_M, res = s_res, mb = s_M * c;
+  const T* base = logits + (int64_t)row * row_stride;
+  const int e0 = s_chunk * chunk_len, e1 = min(vocab, e0 + chunk_len);
+  // this thread's contiguous slice [a0, a1) of the chunk, N-aligned
+  const int per = ((e1 - e0 + kThreads - 1) / kThreads + N - 1) / N * N;
+  const int a0 = min(e1, e0 + tid * per), a1 = min(e1, a0 + per);
+  auto weight = [&](float x) __attribute__((always_inline)) { return exp2_fast(__builtin_fmaf(x, c, -mb)); };
+  float sum = 0.f;
+  int last_pos = -1;
+  const int vend = kVector ? a0 + (a1 - a0) / N * N : a0;   // end of whole vectors of the slice
+  if (kVector) {
+#pragma unroll 4
+    for (int v = a0; v < vend; v += N) {
+      float x[N];
+      Vec<T>::unpack(Vec<T>::load(base + v), x);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float q = weight(x[j]);
+        sum += q;
+        last_pos = q > 0.f ? v + j : last_pos;
+      }
+    }
+  }
+  for (int v = vend; v < a1; ++v) {   // the slice's scalar part (all of it without vector loads)
+    const float q = weight(Vec<T>::scalar(base + v));
+    sum += q;
+    last_pos = q > 0.f ? v : last_pos;
+  }
+  // exclusive scan of the slice sums (thread order = id order)
+  float incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  atomicMax(&s_last, last_pos);
+  __syncthreads();
+  float pre = incl - sum;
+  for (int w = 0; w < wave; ++w) pre += s_wsum[w];
+  if (pre <= res && res < pre + sum) {
+    // Rescan the slice in id order for the first running sum past the target:
+    // whole vectors four loads at a time (the slice was just read: cache hits),
+    // the running sum kept per vector, then the elements of the crossing vector.
+    float run = pre;
+    int hit = -1;
+    int v = a0;
+    for (; v < vend && hit < 0; v += 4 * N) {
+      float vs[4];
+      float xs[4][N];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v + i * N < vend) Vec<T>::unpack(Vec<T>::load(base + v + i * N), xs[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vs[i] = 0.f;
+        if (v + i * N < vend)
+#pragma unroll
+          for (int j = 0; j < N; ++j) vs[i] += weight(xs[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (hit < 0 && v + i * N < vend) {
+          if (run + vs[i] > res) {
+            float r2 = run;
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+              r2 += weight(xs[i][j]);
+              if (hit < 0 && r2 > res) hit = v + i * N + j;
+            }
+            if (hit < 0) hit = v + i * N + N - 1;   // rounding: the vector's last id
+          }
+          run += vs[i];
+        }
+      }
+    }
+    for (int e = vend; e < a1 && hit < 0; ++e) {   // the slice's scalar tail
+      run += weight(Vec<T>::scalar(base + e));
+      if (run > res) hit = e;
+    }
+    atomicMin(&s_found, hit >= 0 ? hit : a1 - 1);   // one thread brackets the target; min guards ties
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // the bracketing id; else (rounding) the chunk's last id of positive weight; else the argmax
+    const int id = s_found != 0x7fffffff ? s_found : (s_last >= 0 ? s_last : s_idx);
+    row_pred[row] = id;
+    row_conf[row] = weight(Vec<T>::scalar(base + id)) / s_S;
+  }
+}
+
+hipError_t launch_decide(const void* part, int nchunk, const float* row_conf, const int32_t* row_pred,
+                         const CommitArgs& a, hipStream_t st) {
+  // Rows with many partials (the fused projection: one per workgroup) get 32 threads each.
+  const Partial* pp = reinterpret_cast<const Partial*>(part);
+  if (nchunk >= 64)
+    hipLaunchKernelGGL((commit_decide<32, 1024>), dim3(a.n_seq), dim3(1024), 0, st, pp, nchunk, row_conf, row_pred,
+                       a.blk_len, a.threshold, a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred,
+                       a.n_committed, a.n_masked_left);
+  else
+    hipLaunchKernelGGL((commit_decide<kDecideLanes, kThreads>), dim3(a.n_seq), dim3(kThreads), 0, st, pp, nchunk,
+                       row_conf, row_pred, a.blk_len, a.threshold, a.thresholds, a.fallback_top1, a.tokens,
+                       a.masked, a.conf, a.pred, a.n_committed, a.n_masked_left);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t commit_sampled_workspace_bytes(int n_seq, int blk_len, int vocab) {
+  const long long rows = (long long)n_seq * blk_len;
+  const int len = commit_chunk_len(rows, vocab, kSampleTargetWGs);
+  return (size_t)rows * ((vocab + len - 1) / len) * sizeof(Partial) + (size_t)rows * 8;
+}
+
+hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
+                                 hipStream_t st) {
+  const int64_t rows = (int64_t)a.n_seq * a.blk_len;
+  const int chunk_len = commit_chunk_len(rows, a.vocab, kSampleTargetWGs);
+  const int nchunk = (a.vocab + chunk_len - 1) / chunk_len;
+  Partial* part = reinterpret_cast<Partial*>(a.ws);
+  float* row_conf = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + (size_t)rows * nchunk * sizeof(Partial));
+  int32_t* row_pred = reinterpret_cast<int32_t*>(row_conf + rows);
+  const float c = kLog2e / temperature;
+  const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32), tl = (uint32_t)step, th = (uint32_t)(step >> 32);
+  const int elem = a.is_bf16 ? 2 : 4;
+  const bool vec = ((uintptr_t)a.logits % 16 == 0) && ((a.row_stride * elem) % 16 == 0);
+  const dim3 grid((unsigned)(rows * nchunk)), rgrid((unsigned)rows), block(kThreads);
+  if (a.is_bf16) {
+    const uint16_t* lg = reinterpret_cast<const uint16_t*>(a.logits);
+    if (vec) {
+      hipLaunchKernelGGL((commit_reduce<uint16_t, true>), grid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c);
+      hipLaunchKernelGGL((sample_locate<uint16_t, true>), rgrid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c, sl, sh, tl, th, row_conf, row_pred);
+    } else {
+      hipLaunchKernelGGL((commit_reduce<uint16_t, false>), grid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c);
+      hipLaunchKernelGGL((sample_locate<uint16_t, false>), rgrid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c, sl, sh, tl, th, row_conf, row_pred);
+    }
+  } else {
+    const float* lg = reinterpret_cast<const float*>(a.logits);
+    if (vec) {
+      hipLaunchKernelGGL((commit_reduce<float, true>), grid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c);
+      hipLaunchKernelGGL((sample_locate<float, true>), rgrid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c, sl, sh, tl, th, row_conf, row_pred);
+    } else {
+      hipLaunchKernelGGL((commit_reduce<float, false>), grid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c);
+      hipLaunchKernelGGL((sample_locate<float, false>), rgrid, block, 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, c, sl, sh, tl, th, row_conf, row_pred);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decide(part, nchunk, row_conf, row_pred, a, st);
+}
 
 int commit_chunks_per_row(long long rows, int vocab) {
   const int len = commit_chunk_len(rows, vocab);
@@ -306,12 +585,12 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(rows * nchunk));
   if (a.is_bf16) {
     const uint16_t* lg = reinterpret_cast<const uint16_t*>(a.logits);
-    if (vec) hipLaunchKernelGGL((commit_reduce<uint16_t, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
-    else hipLaunchKernelGGL((commit_reduce<uint16_t, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
+    if (vec) hipLaunchKernelGGL((commit_reduce<uint16_t, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, kLog2e);
+    else hipLaunchKernelGGL((commit_reduce<uint16_t, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, kLog2e);
   } else {
     const float* lg = reinterpret_cast<const float*>(a.logits);
-    if (vec) hipLaunchKernelGGL((commit_reduce<float, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
-    else hipLaunchKernelGGL((commit_reduce<float, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part);
+    if (vec) hipLaunchKernelGGL((commit_reduce<float, true>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, kLog2e);
+    else hipLaunchKernelGGL((commit_reduce<float, false>), grid, dim3(kThreads), 0, st, lg, a.row_stride, a.vocab, nchunk, chunk_len, a.masked, part, kLog2e);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -319,17 +598,8 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st) {
-  // Rows with many partials (the fused projection: one per workgroup) get 32 threads each.
-  const Partial* pp = reinterpret_cast<const Partial*>(part);
-  if (nchunk >= 64)
-    hipLaunchKernelGGL((commit_decide<32, 1024>), dim3(a.n_seq), dim3(1024), 0, st, pp, nchunk, a.blk_len,
-                       a.threshold, a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred,
-                       a.n_committed, a.n_masked_left);
-  else
-    hipLaunchKernelGGL((commit_decide<kDecideLanes, kThreads>), dim3(a.n_seq), dim3(kThreads), 0, st, pp, nchunk,
-                       a.blk_len, a.threshold, a.thresholds, a.fallback_top1, a.tokens, a.masked, a.conf, a.pred,
-                       a.n_committed, a.n_masked_left);
-  return hipGetLastError();
+  return launch_decide(part, nchunk, nullptr, nullptr, a, st);
 }
+
 
 }  // namespace bd

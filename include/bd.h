@@ -195,6 +195,36 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
                                        size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Confidence commit with sampled predictions.  The pages decode with
+ * temperature 1.0, top-k 0 and top-p 1.0 (digest, method step 6): tokens drawn
+ * from the full softmax with no truncation.  bd_confidence_commit takes the
+ * argmax; this call samples:
+ *
+ *   p_v = softmax(logits[r] / temperature)_v over the whole vocabulary;
+ *   u   = (w + 1/2) / 2^32, w = word 0 of Philox4x32-10 (Salmon et al., SC
+ *         2011) of counter (r, step mod 2^32, step >> 32, 0) under key
+ *         (seed mod 2^32, seed >> 32);
+ *   pred[r] = the first id v whose cumulative probability sum_{w<=v} p_w
+ *         exceeds u (inverse-CDF sampling in id order);
+ *   conf[r] = p_pred.
+ * Then the threshold rule, the fallback and the state update of
+ * bd_confidence_commit.  Invalid rows as there (conf NaN, pred -1).
+ *   temperature > 0 and finite (BD_ERR_VALUE otherwise); a new `step` per
+ *   denoising step gives fresh draws; the same (seed, step) repeats them.
+ *   workspace of bd_confidence_commit_sampled_workspace_size() bytes;
+ *   contents on entry are ignored.  Other arguments as bd_confidence_commit.
+ * The id is found by rescanning, for each masked row, only the vocabulary
+ * chunk in which the running sum passes u (one extra read of 1/k of the row
+ * for k chunks per row).
+ * ---------------------------------------------------------------------- */
+size_t bd_confidence_commit_sampled_workspace_size(int n_seq, int blk_len, int vocab);
+bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step,
+                                       float threshold, bd_fallback fallback, int32_t* tokens, uint8_t* masked,
+                                       float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
+                                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Output projection fused with the confidence commit.  The commit acts on the
  * prediction of each masked position (digest, method step 4), the decoder's
  * distribution over the shared vocabulary (method step 1): the softmax of the

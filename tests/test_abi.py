@@ -22,7 +22,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L.lib, n), n
     assert set(names) == set(L.EXPORTS)
@@ -131,6 +131,28 @@ def test_commit_validation():
     assert call_rw(T=2048) == L.BD_ERR_UNSUPPORTED
     assert call_rw(fb=7) == L.BD_ERR_VALUE
     assert call_rw(nb=ws - 16) == L.BD_ERR_WORKSPACE
+
+
+def test_sampled_commit_validation():
+    ws = L.lib.bd_confidence_commit_sampled_workspace_size(2, 32, 151936)
+    assert ws >= L.lib.bd_confidence_commit_workspace_size(2, 32, 151936) + 64 * 8   # finer chunks, + (conf, id)
+
+    def call(**kw):
+        a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, tau=1.0, seed=5, step=0, thr=0.95,
+                 fb=1, tok=FAKE, msk=FAKE, ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_confidence_commit_sampled(a["lg"], a["stride"], a["n"], a["T"], a["V"], a["dt"], a["tau"],
+                                                  a["seed"], a["step"], a["thr"], a["fb"], a["tok"], a["msk"], None,
+                                                  None, None, None, a["ws"], a["nb"], None)
+    assert call(lg=None) == L.BD_ERR_NULL
+    assert call(stride=100) == L.BD_ERR_SHAPE
+    assert call(tau=0.0) == L.BD_ERR_VALUE
+    assert call(tau=-1.0) == L.BD_ERR_VALUE
+    assert call(tau=math.inf) == L.BD_ERR_VALUE
+    assert call(tau=math.nan) == L.BD_ERR_VALUE
+    assert call(thr=math.nan) == L.BD_ERR_VALUE
+    assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+    assert call(seed=2**64 - 1, step=2**63, nb=0) == L.BD_ERR_WORKSPACE    # 64-bit arguments pass through
 
 
 def test_lmhead_validation():

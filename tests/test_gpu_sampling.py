@@ -1,0 +1,173 @@
+"""GPU parity of bd_confidence_commit_sampled against oracle.sampling.
+
+Both sides draw the same uniform u per row (Philox4x32-10 of (row, step) under the seed) and take
+the first id whose cumulative probability exceeds u.  The GPU sums the probabilities in fp32 (by
+chunks, then within one chunk); the oracle in fp64 in id order.  So:
+  * the sampled id equals the oracle's, except when u lies within 2e-5 of the cumulative boundary
+    between the two ids (fp32 sums over up to 151936 terms, plus the fp32 rounding of u); such
+    rows are counted and must be adjacent in that sense;
+  * conf equals the oracle's probability of the GPU's id to 1e-5 relative;
+  * the commit decision (threshold, fallback, state update) is then bit-exact against the oracle's
+    rule applied to those (conf, id), outside the 1e-4 near-T band.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_decoding_amd as bd
+import workloads as W
+from oracle import commit as C
+from oracle import sampling as S
+from gpu_util import banner, dev, grade_commit, host_vals
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(logits_np, dtype, tokens, masked, blk_len, T, tau, seed, step, fallback=True, stride=None):
+    V = logits_np.shape[1]
+    lg = dev(logits_np, dtype)
+    if stride is not None:
+        pad = torch.zeros((lg.shape[0], stride), dtype=lg.dtype, device=lg.device)
+        pad[:, :V] = lg
+        lg = pad
+    tok = torch.from_numpy(tokens.copy()).cuda()
+    msk = torch.from_numpy(masked.copy()).cuda()
+    out = bd.bd_confidence_commit_sampled(lg, tok, msk, blk_len, T, temperature=tau, seed=seed, step=step,
+                                          fallback=bd.BD_FALLBACK_TOP1 if fallback else bd.BD_FALLBACK_NONE,
+                                          vocab=V)
+    torch.cuda.synchronize()
+    gpu = {"tokens": tok.cpu().numpy(), "masked": msk.cpu().numpy(),
+           "conf": out["conf"].cpu().numpy().astype(np.float64), "pred": out["pred"].cpu().numpy(),
+           "n_committed": out["n_committed"].cpu().numpy(), "n_masked_left": out["n_masked_left"].cpu().numpy()}
+    x = host_vals(logits_np, dtype)[:, :V]
+    ref = S.sampled_commit(x, tokens, masked, blk_len, T, tau, seed, step,
+                           C.FALLBACK_TOP1 if fallback else C.FALLBACK_NONE)
+    conf_o = np.full(len(tokens), np.nan)
+    boundary = 0
+    for r in np.flatnonzero(masked):
+        g, o = int(gpu["pred"][r]), int(ref["pred"][r])
+        assert (g < 0) == (o < 0), f"row {r}: invalid flags differ"
+        if g < 0:
+            continue
+        row = np.asarray(x[r], dtype=np.float64)
+        p = np.exp((row - row.max()) / tau)
+        p /= p.sum()
+        if g != o:
+            cum = np.cumsum(p)
+            lo, hi = (cum[g - 1] if g > 0 else 0.0), cum[g]
+            u = ref["u"][r]
+            assert p[g] > 0 and lo - 2e-5 <= u <= hi + 2e-5, f"row {r}: id {g} vs {o}, u={u} outside [{lo}, {hi}]"
+            boundary += 1
+        conf_o[r] = p[g]
+        assert abs(gpu["conf"][r] - p[g]) <= 1e-5 * p[g] + 1e-9, f"row {r}: conf {gpu['conf'][r]} vs {p[g]}"
+    # tail ids have probabilities ~1e-6 apart, comparable to the fp32 sums: some boundary rows are
+    # expected; each one was checked above, a wholesale mismatch would not pass this
+    assert boundary <= max(2, int(0.05 * masked.sum())), f"{boundary} boundary rows"
+    rule = C.decide(conf_o, np.where(gpu["pred"] >= 0, gpu["pred"], -1).astype(np.int32), tokens, masked, blk_len,
+                    T, C.FALLBACK_TOP1 if fallback else C.FALLBACK_NONE)
+    near, amb = grade_commit(rule, gpu, masked, tokens, blk_len, T, fallback)
+    print(f"  tau={tau} T={T} seed={seed} step={step}: committed={int(rule['committed'].sum())} "
+          f"near-T={near} ambiguous={amb} boundary ids={boundary}")
+    return gpu, ref
+
+
+def test_tiny_f32_workload():
+    wl = W.WORKLOADS["tiny_f32"]
+    banner("sampled commit tiny_f32")
+    c = W.commit_inputs(1, 32, wl.vocab, "f32", wl.seed, masked_frac=0.5, logit_std=wl.logit_std)
+    for tau in (1.0, 0.7):
+        for T in (wl.threshold, 0.3, 0.1):
+            for step in (0, 1):
+                run_case(c["logits"], "f32", c["tokens"], c["masked"], 32, T, tau, seed=17, step=step)
+
+
+def test_decode_step_workload():
+    wl = W.WORKLOADS["decode_step_bf16"]
+    banner("sampled commit decode_step_bf16")
+    c = W.commit_inputs(1, 32, wl.vocab, "bf16", wl.seed, boost=wl.boost)
+    for T in (0.95, 0.5):
+        for seed, step in ((1, 0), (2, 5), (2**40 + 3, 2**33 + 1)):
+            run_case(c["logits"], "bf16", c["tokens"], c["masked"], 32, T, 1.0, seed, step)
+
+
+@pytest.mark.parametrize("V,stride", [(5003, None), (5003, 5008), (4096, 4100), (77, None)])
+def test_ragged_vocab_and_strides(V, stride):
+    banner(f"sampled commit V={V} stride={stride}")
+    c = W.commit_inputs(4, 32, V, "bf16", seed=V, masked_frac=0.75, boost=(0.0, 9.0))
+    run_case(c["logits"], "bf16", c["tokens"], c["masked"], 32, 0.4, 1.0, seed=3, step=9, stride=stride)
+    c = W.commit_inputs(2, 32, V, "f32", seed=V + 1, masked_frac=0.75, logit_std=2.5)
+    run_case(c["logits"], "f32", c["tokens"], c["masked"], 32, 0.2, 0.8, seed=4, step=1, stride=stride)
+
+
+def test_invalid_rows_and_neg_inf():
+    banner("sampled commit invalid rows")
+    rng = np.random.default_rng(9)
+    V, blk = 3000, 8
+    x = rng.standard_normal((2 * blk, V)).astype(np.float32)
+    x[0, 17] = np.nan
+    x[1, 2999] = np.inf
+    x[2, :] = -np.inf
+    x[3, :2500] = -np.inf
+    x[4, ::2] = -np.inf
+    x[5, 1:] = -np.inf
+    masked = np.ones(2 * blk, np.uint8)
+    tokens = np.full(2 * blk, -1, np.int32)
+    for dt, arr in (("bf16", W.f32_to_bf16_bits(x)), ("f32", x)):
+        gpu, _ = run_case(arr, dt, tokens, masked, blk, 0.5, 1.0, seed=5, step=0)
+        assert gpu["pred"][5] == 0 and abs(gpu["conf"][5] - 1.0) < 1e-6
+        assert gpu["pred"][4] % 2 == 1 and gpu["pred"][3] >= 2500
+
+
+def test_batched_loop_scale():
+    wl = W.WORKLOADS["decode_loop_bf16"]
+    banner("sampled commit 64 x 32 x 151936")
+    rng = np.random.default_rng(wl.seed)
+    bits = W.boosted_logits_bits(64 * 32, wl.vocab, wl.boost[0], wl.boost[1], rng)
+    masked = (rng.random(64 * 32) < 0.6).astype(np.uint8)
+    tokens = np.where(masked == 1, -1, 5).astype(np.int32)
+    run_case(bits, "bf16", tokens, masked, 32, 0.95, 1.0, seed=21, step=3)
+
+
+def test_sample_frequencies_match_the_distribution():
+    """2048 rows holding the same 40 logits draw 2048 independent samples (each row has its own
+    counter): their frequencies follow softmax(logits / tau) (chi-square), at two temperatures."""
+    banner("sampled commit frequencies")
+    rng = np.random.default_rng(13)
+    base = (rng.standard_normal(40) * 1.5).astype(np.float32)
+    rows = 2048
+    x = np.repeat(base[None], rows, axis=0)
+    masked = np.ones(rows, np.uint8)
+    tokens = np.full(rows, -1, np.int32)
+    for tau in (1.0, 2.0):
+        lg = torch.from_numpy(x).cuda()
+        tok = torch.from_numpy(tokens.copy()).cuda()
+        msk = torch.from_numpy(masked.copy()).cuda()
+        out = bd.bd_confidence_commit_sampled(lg, tok, msk, 32, 2.0, temperature=tau, seed=99, step=7,
+                                              fallback=bd.BD_FALLBACK_NONE)
+        pred = out["pred"].cpu().numpy()
+        p = np.exp((base.astype(np.float64) - base.max()) / tau)
+        p /= p.sum()
+        counts = np.bincount(pred, minlength=40)
+        keep = rows * p >= 5
+        chi2 = float(((counts[keep] - rows * p[keep]) ** 2 / (rows * p[keep])).sum()) + \
+            float(((counts[~keep].sum() - rows * p[~keep].sum()) ** 2 / max(rows * p[~keep].sum(), 1e-9)))
+        dof = int(keep.sum())
+        print(f"  tau={tau}: chi2={chi2:.1f} over {dof} cells")
+        assert chi2 < dof + 6 * np.sqrt(2 * dof)
+        # nothing passes T = 2 and the fallback is off: the state is unchanged
+        assert (msk.cpu().numpy() == 1).all()
+
+
+def test_reproducible_and_fresh_per_step():
+    banner("sampled commit reproducibility")
+    c = W.commit_inputs(2, 32, 2000, "bf16", seed=8, masked_frac=1.0, logit_std=1.0)
+    lg = dev(c["logits"], "bf16")
+
+    def draw(step):
+        tok = torch.from_numpy(c["tokens"].copy()).cuda()
+        msk = torch.from_numpy(c["masked"].copy()).cuda()
+        return bd.bd_confidence_commit_sampled(lg, tok, msk, 32, 2.0, seed=1234, step=step,
+                                               fallback=bd.BD_FALLBACK_NONE)["pred"].cpu().numpy()
+    a, b, d = draw(4), draw(4), draw(5)
+    assert np.array_equal(a, b)
+    assert (a != d).mean() > 0.5
