@@ -35,10 +35,12 @@ Modules:
   hidden x weight^T), for the fused projection + confidence kernel.
 * :mod:`oracle.sampling` -- the commit with sampled predictions (temperature,
   inverse-CDF sampling from a counter-based generator).
+* :mod:`oracle.paged` -- the prefix cache in pages (gather through the page
+  table, append a finished block).
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than
 itself (library routines in special cases, closed forms, invariants, brute
 force and finite differences).  No function here is "parity unpinned".
 """
 
-from . import attention, commit, decode_loop, lmhead, sampling  # noqa: F401
+from . import attention, commit, decode_loop, lmhead, paged, sampling  # noqa: F401
