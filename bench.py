@@ -279,6 +279,36 @@ def main():
 
     loops = [full_loop(T) for T in lw.thresholds]
 
+    # the same decode step with the prefix in shuffled pages of 256 rows (bd_attn_decode_block_paged)
+    page = 256
+    max_pages = (max_p + page - 1) // page
+    pstart_np = ps.cpu().numpy()
+    prng = np.random.default_rng(lw.seed + 11)
+    table_np = prng.permutation(lw.n_seq * max_pages).astype(np.int32).reshape(lw.n_seq, max_pages)
+    src_rows, dst_rows = [], []
+    for s_ in range(lw.n_seq):
+        P_ = int(plen[s_])
+        j_ = np.arange(P_)
+        src_rows.append(int(pstart_np[s_]) + j_)
+        dst_rows.append(table_np[s_, j_ // page].astype(np.int64) * page + j_ % page)
+    src_t = torch.from_numpy(np.concatenate(src_rows)).to(dev)
+    dst_t = torch.from_numpy(np.concatenate(dst_rows)).to(dev)
+    kpg = torch.zeros((lw.n_seq * max_pages * page, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vpg = torch.zeros_like(kpg)
+    kpg[dst_t] = kc[src_t]
+    vpg[dst_t] = vc[src_t]
+    del src_t, dst_t
+    table_t = torch.from_numpy(table_np).to(dev)
+    pl32 = pl.to(torch.int32)
+    pg_us = []
+    for rnd in range(4):
+        t_us = primed([lambda: bd.bd_attn_decode_block_paged(qb, kb, vb, kpg, vpg, table_t, page, pl32, max_p,
+                                                             o=dec_o, lse=dec_lse, workspace=dec_ws)
+                       for _ in range(8)])
+        if rnd:
+            pg_us.extend(t_us)
+    del kpg, vpg
+
     # per-position thresholds (bd_confidence_commit_rowwise) on the all-masked first step
     thr_rows = torch.from_numpy(np.random.default_rng(lw.seed + 7).uniform(0.5, 0.99, n_rows)
                                 .astype(np.float32)).to(dev)
@@ -420,6 +450,8 @@ def main():
         "decode_loop": {"kv_GB_per_step": round(kv_bytes_loop / 1e9, 3),
                         "attn_us_median": round(float(np.median(dec_ms)) * 1e3, 1),
                         "attn_GBps": round(kv_bytes_loop / (np.median(dec_ms) * 1e-3) / 1e9, 1),
+                        "attn_paged256_us_median": round(float(np.median(pg_us)), 1),
+                        "attn_paged256_GBps": round(kv_bytes_loop / (np.median(pg_us) * 1e-6) / 1e9, 1),
                         "commit_GBps_first_step": round(com_gbs_loop[0], 1),
                         "commit_GBps_median": round(float(np.median(com_gbs_loop)), 1),
                         "commit_rowwise_GBps_first_step": round(rw_bytes / (np.median(rw_us) * 1e-6) / 1e9, 1),

@@ -19,6 +19,7 @@ __all__ = [
     "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
     "bd_confidence_commit_rowwise", "bd_lmhead_commit", "bd_lmhead_commit_workspace_size",
     "bd_confidence_commit_sampled", "bd_confidence_commit_sampled_workspace_size",
+    "bd_attn_decode_block_paged", "bd_kv_append_block",
     "bd_attn_bwd_workspace_size", "bd_attn_decode_workspace_size", "bd_confidence_commit_workspace_size",
     "BdError", "BD_F32", "BD_BF16", "BD_FALLBACK_NONE", "BD_FALLBACK_TOP1", "lib",
 ]
@@ -253,3 +254,46 @@ def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold
                                           _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
     check(st, "bd_confidence_commit_sampled")
     return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}
+
+
+def bd_attn_decode_block_paged(q_blk, k_blk, v_blk, k_pages, v_pages, block_table, page_size: int, prefix_len,
+                               max_prefix_len: int, softmax_scale: float = 0.0, o=None, lse=None, workspace=None,
+                               stream=None):
+    """One block against a paged prefix cache.  q_blk [n_seq, T, Hq, d], k_blk/v_blk [n_seq, T, Hkv, d],
+    k_pages/v_pages [n_pages * page_size, Hkv, d] (bf16), block_table int32 [n_seq, max_pages],
+    prefix_len int32 [n_seq].  Returns (o, lse)."""
+    n_seq, T, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    for t, name in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, dtype=torch.bfloat16)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(prefix_len, "prefix_len", (n_seq,), torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != n_seq:
+        raise ValueError("block_table must be [n_seq, max_pages]")
+    dev = q_blk.device
+    o = torch.empty_like(q_blk) if o is None else o
+    lse = torch.empty((n_seq, Hq, T), dtype=torch.float32, device=dev) if lse is None else lse
+    ws, nb = _workspace(bd_attn_decode_workspace_size(n_seq, T, max_prefix_len, Hq, Hkv, d), dev, workspace)
+    st = lib.bd_attn_decode_block_paged(_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pages), _ptr(v_pages),
+                                        _ptr(block_table), block_table.shape[1], page_size, _ptr(prefix_len),
+                                        max_prefix_len, _ptr(o), _ptr(lse), n_seq, T, Hq, Hkv, d,
+                                        float(softmax_scale), BD_BF16, _ptr(ws), nb, _stream(stream))
+    check(st, "bd_attn_decode_block_paged")
+    return o, lse
+
+
+def bd_kv_append_block(k_blk, v_blk, k_pages, v_pages, block_table, page_size: int, prefix_len, n_masked_left=None,
+                       stream=None):
+    """Append finished blocks (n_masked_left == 0, or all) to the paged cache; prefix_len grows in place."""
+    n_seq, T, Hkv, d = k_blk.shape
+    for t, name in ((k_blk, "k_blk"), (v_blk, "v_blk"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, dtype=torch.bfloat16)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(prefix_len, "prefix_len", (n_seq,), torch.int32)
+    if n_masked_left is not None:
+        _need(n_masked_left, "n_masked_left", (n_seq,), torch.int32)
+    st = lib.bd_kv_append_block(_ptr(k_blk), _ptr(v_blk), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                block_table.shape[1], page_size, _ptr(prefix_len),
+                                _ptr(n_masked_left) if n_masked_left is not None else None, n_seq, T, Hkv, d, BD_BF16,
+                                _stream(stream))
+    check(st, "bd_kv_append_block")

@@ -83,8 +83,10 @@ struct DecParams {
   const uint16_t* v_blk;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
-  const int64_t* prefix_start;
+  const int64_t* prefix_start;  // packed cache: first row of each sequence's prefix
   const int32_t* prefix_len;
+  const int32_t* block_table;   // paged cache: [n_seq][max_pages] page of each page_size-key span
+  int max_pages, page_size;
   float2* part_ml;   // [lane][R + n_seq][kRows]: (m, l) of each partial row
   uint16_t* part_o;  // [lane][R + n_seq][wave][dp][lane of wave][8]: bf16 O / l of each partial
   uint16_t* o;
@@ -169,6 +171,12 @@ struct Cursor {
   int64_t start;
 };
 
+// kPaged: the prefix lives in pages of page_size rows (a multiple of the
+// 32-key tile, so a tile of the prefix lies in one page): prefix row j of
+// sequence s is row block_table[s][j / page_size] * page_size + j % page_size
+// of the page buffer.  Otherwise it is row prefix_start[s] + j of the packed
+// cache.
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -216,8 +224,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     c.j = __builtin_amdgcn_readfirstlane(j);
     c.P = ((c_i32*)(uintptr_t)p.prefix_len)[c.s];
     c.tiles = (c.P + p.blk_len + KT - 1) / KT;
-    c.start = ((c_i64*)(uintptr_t)p.prefix_start)[c.s];
+    c.start = kPaged ? 0 : ((c_i64*)(uintptr_t)p.prefix_start)[c.s];
     return c;
+  };
+  // Physical cache row of prefix row j of sequence s (uniform j: a scalar load of the table).
+  auto prow_uniform = [&](int s, int j) __attribute__((always_inline)) -> int64_t {
+    const int pg = ((c_i32*)(uintptr_t)p.block_table)[(int64_t)s * p.max_pages + j / p.page_size];
+    return (int64_t)pg * p.page_size + j % p.page_size;
+  };
+  auto prow_lane = [&](int s, int j) __attribute__((always_inline)) -> int64_t {
+    const int pg = p.block_table[(int64_t)s * p.max_pages + j / p.page_size];
+    return (int64_t)pg * p.page_size + j % p.page_size;
   };
   auto advance = [&](Cursor& c) {
     if (++c.j == c.tiles && c.s + 1 < p.n_seq) c = cursor_at(c.s + 1, 0);
@@ -245,7 +262,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   auto fetch = [&](Staged& sg, bool adv) __attribute__((always_inline)) {
     const int key0 = ld.j * KT, kend = ld.P + p.blk_len;
     if (key0 + KT <= ld.P) {
-      const int64_t row0 = (ld.start + key0) * rs + (int64_t)kvh * D;
+      const int64_t prow0 = kPaged ? prow_uniform(ld.s, key0) : ld.start + key0;
+      const int64_t row0 = prow0 * rs + (int64_t)kvh * D;
       const char* kg = reinterpret_cast<const char*>(p.k_cache + row0);
       const char* vg = reinterpret_cast<const char*>(p.v_cache + row0);
 #pragma unroll
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int rr = 4 * nn + (lane >> 4);
         const int c = (lane & 15) ^ tile_swz(rr);
         const int j = min(key0 + rr, kend - 1);
-        const int64_t grow = j < ld.P ? (ld.start + j) : -1;
+        const int64_t grow = j < ld.P ? (kPaged ? prow_lane(ld.s, j) : ld.start + j) : -1;
         const int64_t brow = ((int64_t)ld.s * p.blk_len + (j - ld.P));
         const uint16_t* ksrc = (grow >= 0 ? p.k_cache + grow * rs : p.k_blk + brow * rs) + kvh * D + 8 * c;
         const uint16_t* vsrc = (grow >= 0 ? p.v_cache + grow * rs : p.v_blk + brow * rs) + kvh * D + 8 * c;
@@ -624,14 +642,20 @@ size_t decode_workspace_bytes(const DecodeShape& s, int /*is_bf16*/) {
   return part_slots(s, pl) * (sizeof(float2) + D * sizeof(uint16_t));
 }
 
-hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
-                              const void* v_cache, const int64_t* prefix_start, const int32_t* prefix_len,
-                              void* o, float* lse, void* ws, const DecodeShape& s, hipStream_t st) {
+namespace {
+
+hipError_t launch_decode_impl(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
+                              const void* v_cache, const int64_t* prefix_start, const int32_t* block_table,
+                              int max_pages, int page_size, const int32_t* prefix_len, void* o, float* lse,
+                              void* ws, const DecodeShape& s, hipStream_t st) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split<false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
   });
   if (attr_err != hipSuccess) return attr_err;
   const Plan pl = make_plan(s);
@@ -644,6 +668,9 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   p.v_cache = static_cast<const uint16_t*>(v_cache);
   p.prefix_start = prefix_start;
   p.prefix_len = prefix_len;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
   p.part_ml = reinterpret_cast<float2*>(ws);
   p.part_o = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + slots * sizeof(float2));
   p.o = static_cast<uint16_t*>(o);
@@ -657,10 +684,70 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
   p.row_tiles = pl.row_tiles;
   p.R = pl.R;
   p.scale_log2 = s.scale * kLog2e;
-  hipLaunchKernelGGL(decode_split, dim3((unsigned)((long long)pl.R * pl.lanes)), dim3(kThreads), kSmemBytes, st, p);
+  const dim3 grid((unsigned)((long long)pl.R * pl.lanes));
+  if (block_table) hipLaunchKernelGGL(decode_split<true>, grid, dim3(kThreads), kSmemBytes, st, p);
+  else hipLaunchKernelGGL(decode_split<false>, grid, dim3(kThreads), kSmemBytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge, dim3((unsigned)((long long)s.n_seq * pl.lanes * kNW)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// Append each finished block (n_masked_left[s] == 0, or every block without
+// that array) to its sequence's pages: rows t of the block's K and V go to
+// prefix row prefix_len[s] + t; then prefix_len[s] grows by blk_len.  One
+// workgroup per sequence; 16-byte copies.  A block whose rows would pass the
+// sequence's last page is left out (the caller allocates pages first).
+__global__ __launch_bounds__(256) void kv_append(const uint16_t* __restrict__ k_blk,
+                                                 const uint16_t* __restrict__ v_blk, uint16_t* __restrict__ k_pages,
+                                                 uint16_t* __restrict__ v_pages,
+                                                 const int32_t* __restrict__ block_table, int max_pages,
+                                                 int page_size, int32_t* __restrict__ prefix_len,
+                                                 const int32_t* __restrict__ n_masked_left, int blk_len,
+                                                 int row_elems) {
+  const int s = blockIdx.x;
+  if (n_masked_left && n_masked_left[s] != 0) return;
+  const int P = prefix_len[s];
+  if ((int64_t)P + blk_len > (int64_t)max_pages * page_size) return;
+  const int per_row = row_elems / 8;   // 16-byte pieces per row
+  for (int c = threadIdx.x; c < blk_len * per_row; c += blockDim.x) {
+    const int t = c / per_row, k8 = c - t * per_row;
+    const int j = P + t;
+    const int64_t dst = ((int64_t)block_table[(int64_t)s * max_pages + j / page_size] * page_size + j % page_size) *
+                            row_elems + k8 * 8;
+    const int64_t src = ((int64_t)s * blk_len + t) * row_elems + k8 * 8;
+    *reinterpret_cast<uint4*>(k_pages + dst) = *reinterpret_cast<const uint4*>(k_blk + src);
+    *reinterpret_cast<uint4*>(v_pages + dst) = *reinterpret_cast<const uint4*>(v_blk + src);
+  }
+  __syncthreads();   // every thread has read P
+  if (threadIdx.x == 0) prefix_len[s] = P + blk_len;
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
+                              const void* v_cache, const int64_t* prefix_start, const int32_t* prefix_len,
+                              void* o, float* lse, void* ws, const DecodeShape& s, hipStream_t st) {
+  return launch_decode_impl(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_start, nullptr, 0, 0, prefix_len, o, lse,
+                            ws, s, st);
+}
+
+hipError_t launch_decode_bf16_paged(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pages,
+                                    const void* v_pages, const int32_t* block_table, int max_pages, int page_size,
+                                    const int32_t* prefix_len, void* o, float* lse, void* ws, const DecodeShape& s,
+                                    hipStream_t st) {
+  return launch_decode_impl(q_blk, k_blk, v_blk, k_pages, v_pages, nullptr, block_table, max_pages, page_size,
+                            prefix_len, o, lse, ws, s, st);
+}
+
+hipError_t launch_kv_append_bf16(const void* k_blk, const void* v_blk, void* k_pages, void* v_pages,
+                                 const int32_t* block_table, int max_pages, int page_size, int32_t* prefix_len,
+                                 const int32_t* n_masked_left, int n_seq, int blk_len, int n_kv_heads, int head_dim,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(kv_append, dim3((unsigned)n_seq), dim3(256), 0, st, static_cast<const uint16_t*>(k_blk),
+                     static_cast<const uint16_t*>(v_blk), static_cast<uint16_t*>(k_pages),
+                     static_cast<uint16_t*>(v_pages), block_table, max_pages, page_size, prefix_len, n_masked_left,
+                     blk_len, n_kv_heads * head_dim);
   return hipGetLastError();
 }
 

@@ -166,6 +166,48 @@ bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void*
       static_cast<float*>(o), lse, s, stream));
 }
 
+bd_status bd_attn_decode_block_paged(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pages,
+                                     const void* v_pages, const int32_t* block_table, int max_pages_per_seq,
+                                     int page_size, const int32_t* prefix_len, int max_prefix_len, void* o,
+                                     float* lse, int n_seq, int blk_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                     float softmax_scale, bd_dtype dtype, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!q_blk || !k_blk || !v_blk || !o || !prefix_len) return BD_ERR_NULL;
+  if (max_prefix_len > 0 && (!k_pages || !v_pages || !block_table)) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || max_prefix_len < 0 || max_pages_per_seq < 0) return BD_ERR_SHAPE;
+  if (page_size <= 0 || page_size % 32 != 0) return BD_ERR_UNSUPPORTED;
+  if ((long long)max_pages_per_seq * page_size < max_prefix_len) return BD_ERR_SHAPE;
+  bd_status st = check_attn_shape(n_seq, blk_len, n_q_heads, n_kv_heads, head_dim, 1, dtype, softmax_scale);
+  if (st != BD_OK) return st;
+  if (dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
+  if ((long long)max_prefix_len + blk_len > kMaxGrid / 2) return BD_ERR_SHAPE;
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+      (k_pages && !aligned16(k_pages)) || (v_pages && !aligned16(v_pages)))
+    return BD_ERR_ALIGNMENT;
+  bd::DecodeShape s{n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim,
+                    resolve_scale(softmax_scale, head_dim)};
+  const size_t need = bd::decode_workspace_bytes(s, 1);
+  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  return hip_status(bd::launch_decode_bf16_paged(q_blk, k_blk, v_blk, k_pages, v_pages, block_table,
+                                                 max_pages_per_seq, page_size, prefix_len, o, lse, workspace, s,
+                                                 stream));
+}
+
+bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages, void* v_pages,
+                             const int32_t* block_table, int max_pages_per_seq, int page_size, int32_t* prefix_len,
+                             const int32_t* n_masked_left, int n_seq, int blk_len, int n_kv_heads, int head_dim,
+                             bd_dtype dtype, hipStream_t stream) {
+  if (!k_blk || !v_blk || !k_pages || !v_pages || !block_table || !prefix_len) return BD_ERR_NULL;
+  if (n_seq <= 0 || blk_len <= 0 || n_kv_heads <= 0 || head_dim <= 0 || max_pages_per_seq <= 0) return BD_ERR_SHAPE;
+  if (page_size <= 0) return BD_ERR_SHAPE;
+  if (dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
+  if ((n_kv_heads * head_dim) % 8 != 0) return BD_ERR_UNSUPPORTED;
+  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pages) || !aligned16(v_pages)) return BD_ERR_ALIGNMENT;
+  return hip_status(bd::launch_kv_append_bf16(k_blk, v_blk, k_pages, v_pages, block_table, max_pages_per_seq,
+                                              page_size, prefix_len, n_masked_left, n_seq, blk_len, n_kv_heads,
+                                              head_dim, stream));
+}
+
 size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab) {
   if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
   return bd::commit_workspace_bytes(n_seq, blk_len, vocab);

@@ -37,6 +37,15 @@ hipError_t launch_decode_bf16(const void* q_blk, const void* k_blk, const void* 
                               const void* k_cache, const void* v_cache, const int64_t* prefix_start,
                               const int32_t* prefix_len, void* o, float* lse, void* ws,
                               const DecodeShape& s, hipStream_t st);
+// The same with the prefix in pages (page_size a multiple of 32).
+hipError_t launch_decode_bf16_paged(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pages,
+                                    const void* v_pages, const int32_t* block_table, int max_pages, int page_size,
+                                    const int32_t* prefix_len, void* o, float* lse, void* ws, const DecodeShape& s,
+                                    hipStream_t st);
+hipError_t launch_kv_append_bf16(const void* k_blk, const void* v_blk, void* k_pages, void* v_pages,
+                                 const int32_t* block_table, int max_pages, int page_size, int32_t* prefix_len,
+                                 const int32_t* n_masked_left, int n_seq, int blk_len, int n_kv_heads, int head_dim,
+                                 hipStream_t st);
 hipError_t launch_decode_f32(const float* q_blk, const float* k_blk, const float* v_blk,
                              const float* k_cache, const float* v_cache, const int64_t* prefix_start,
                              const int32_t* prefix_len, float* o, float* lse, const DecodeShape& s,

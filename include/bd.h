@@ -141,6 +141,46 @@ bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void*
                                bd_dtype dtype, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * One block against a prefix cache held in pages (the cache layout of the
+ * serving engines the pages name for the model, SGLang and the Nano-vLLM
+ * adaptation: editorial, "The model, the weights and the serving stack").  The attention is exactly that of
+ * bd_attn_decode_block; only where prefix row j of sequence s lives differs:
+ *
+ *   k_pages, v_pages [n_pages * page_size, n_kv_heads, head_dim] bf16: page p
+ *        holds cache rows p*page_size .. p*page_size + page_size - 1;
+ *   block_table int32[n_seq][max_pages_per_seq] (device): prefix row j of
+ *        sequence s is row block_table[s][j / page_size] * page_size +
+ *        j % page_size;
+ *   page_size a multiple of 32 (BD_ERR_UNSUPPORTED otherwise);
+ *   max_pages_per_seq * page_size >= max_prefix_len (BD_ERR_SHAPE otherwise).
+ * bf16 only.  The workspace is that of bd_attn_decode_block
+ * (bd_attn_decode_workspace_size).  Other arguments as bd_attn_decode_block.
+ * ---------------------------------------------------------------------- */
+bd_status bd_attn_decode_block_paged(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pages,
+                                     const void* v_pages, const int32_t* block_table, int max_pages_per_seq,
+                                     int page_size, const int32_t* prefix_len, int max_prefix_len, void* o,
+                                     float* lse, int n_seq, int blk_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                     float softmax_scale, bd_dtype dtype, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Append finished blocks to the paged cache (digest, novelty paragraph: the
+ * block structure lets later blocks reuse the KV cache of earlier ones).  For
+ * every sequence s with n_masked_left[s] == 0 (every sequence when
+ * n_masked_left is NULL): rows t = 0 .. blk_len-1 of k_blk[s] / v_blk[s]
+ * ([n_seq, blk_len, n_kv_heads, head_dim] bf16) are written to prefix rows
+ * prefix_len[s] + t (addressed as in bd_attn_decode_block_paged), then
+ * prefix_len[s] += blk_len (int32[n_seq], device, in/out).  The caller
+ * allocates the pages first: a block whose rows would pass
+ * max_pages_per_seq * page_size is left out (prefix_len unchanged).
+ * page_size any positive value; bf16 only.
+ * ---------------------------------------------------------------------- */
+bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages, void* v_pages,
+                             const int32_t* block_table, int max_pages_per_seq, int page_size, int32_t* prefix_len,
+                             const int32_t* n_masked_left, int n_seq, int blk_len, int n_kv_heads, int head_dim,
+                             bd_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Confidence-threshold commit (digest, method steps 4 and 6).
  *
  * logits [n_seq * blk_len rows, vocab], row r at logits + r * row_stride

@@ -22,7 +22,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L.lib, n), n
     assert set(names) == set(L.EXPORTS)
@@ -153,6 +153,39 @@ def test_sampled_commit_validation():
     assert call(thr=math.nan) == L.BD_ERR_VALUE
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
     assert call(seed=2**64 - 1, step=2**63, nb=0) == L.BD_ERR_WORKSPACE    # 64-bit arguments pass through
+
+
+def test_paged_validation():
+    ws = L.lib.bd_attn_decode_workspace_size(1, 32, 4096, 16, 8, 128)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, mp=64, ps=64, pl=FAKE, mpl=4096, o=FAKE, n=1,
+                 T=32, hq=16, hkv=8, d=128, sc=0.0, dt=L.BD_BF16, ws=FAKE, nb=ws)
+        a.update(kw)
+        return L.lib.bd_attn_decode_block_paged(a["q"], a["k"], a["v"], a["kp"], a["vp"], a["bt"], a["mp"], a["ps"],
+                                                a["pl"], a["mpl"], a["o"], None, a["n"], a["T"], a["hq"], a["hkv"],
+                                                a["d"], a["sc"], a["dt"], a["ws"], a["nb"], None)
+    assert call(bt=None) == L.BD_ERR_NULL
+    assert call(pl=None) == L.BD_ERR_NULL
+    assert call(ps=48) == L.BD_ERR_UNSUPPORTED
+    assert call(ps=0) == L.BD_ERR_UNSUPPORTED
+    assert call(mp=63) == L.BD_ERR_SHAPE             # 63 pages of 64 rows < 4096
+    assert call(dt=L.BD_F32) == L.BD_ERR_UNSUPPORTED
+    assert call(kp=MIS) == L.BD_ERR_ALIGNMENT
+    assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+
+    def app(**kw):
+        a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, mp=64, ps=64, pl=FAKE, nml=None, n=1, T=32, hkv=8, d=128,
+                 dt=L.BD_BF16)
+        a.update(kw)
+        return L.lib.bd_kv_append_block(a["k"], a["v"], a["kp"], a["vp"], a["bt"], a["mp"], a["ps"], a["pl"],
+                                        a["nml"], a["n"], a["T"], a["hkv"], a["d"], a["dt"], None)
+    assert app(bt=None) == L.BD_ERR_NULL
+    assert app(mp=0) == L.BD_ERR_SHAPE
+    assert app(ps=0) == L.BD_ERR_SHAPE
+    assert app(dt=L.BD_F32) == L.BD_ERR_UNSUPPORTED
+    assert app(hkv=1, d=4) == L.BD_ERR_UNSUPPORTED
+    assert app(kp=MIS) == L.BD_ERR_ALIGNMENT
 
 
 def test_lmhead_validation():
