@@ -415,6 +415,26 @@ def main():
     lm_us, un_us = np.array(lm_us), np.array(un_us)
     lm_bytes = (hw.vocab + hw.block_size) * H_lm * 2
 
+    # ------------------------------- forward at the first training length (12288 tokens)
+    w3 = W.WORKLOADS["fwd_L12288_bf16"]
+    inp3 = W.attention_inputs(w3.batch, w3.seqlen, w3.n_q_heads, w3.n_kv_heads, w3.head_dim, "bf16", w3.seed)
+    q3, k3, v3 = (to_dev(inp3[n]) for n in ("q", "k", "v"))
+    del inp3
+    o3 = torch.empty_like(q3)
+    lse3 = torch.empty((w3.batch, w3.n_q_heads, w3.seqlen), dtype=torch.float32, device=dev)
+    nb3 = w3.seqlen // w3.block_size
+    f3_flops = 4.0 * w3.head_dim * w3.block_size ** 2 * nb3 * (nb3 + 1) / 2 * w3.n_q_heads * w3.batch
+    for _ in range(5):
+        bd.bd_attn_fwd(q3, k3, v3, w3.block_size, o=o3, lse=lse3)
+    f3_ev = [(ev(), ev()) for _ in range(30)]
+    for a, b_ in f3_ev:
+        a.record()
+        bd.bd_attn_fwd(q3, k3, v3, w3.block_size, o=o3, lse=lse3)
+        b_.record()
+    torch.cuda.synchronize()
+    f3_ms = np.array([a.elapsed_time(b_) for a, b_ in f3_ev])
+    del q3, k3, v3, o3, lse3
+
     # --------------------------------------------------------- CPU oracle sample
     cpu = None
     if not args.no_cpu:
@@ -467,6 +487,11 @@ def main():
                                          "GBps": round(lm_bytes / (np.median(lm_us) * 1e-6) / 1e9, 1),
                                          "unfused_us_median": round(float(np.median(un_us)), 2),
                                          "speedup_vs_unfused": round(float(np.median(un_us) / np.median(lm_us)), 3)},
+        "fwd_L12288": {"flops": f3_flops, "ms_median": round(float(np.median(f3_ms)), 4),
+                       "ms_p10": round(float(np.percentile(f3_ms, 10)), 4),
+                       "ms_p90": round(float(np.percentile(f3_ms, 90)), 4),
+                       "TFLOPs": round(f3_flops / (np.median(f3_ms) * 1e-3) / 1e12, 2),
+                       "frac_peak": round(f3_flops / (np.median(f3_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "commit_32x151936": {"bytes": com1_bytes, "us_median": round(float(np.median(com1_us)), 2),
                              "us_p10": round(float(np.percentile(com1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(com1_us, 90)), 2),

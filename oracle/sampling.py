@@ -15,6 +15,22 @@ the sampling reading:
 * confidence = p of the sampled id; the threshold rule, the fallback and the state update are
   those of :func:`oracle.commit.confidence_commit`, with the sampled id in place of the argmax.
 
+Truncation (the pages name the top-k and top-p knobs and switch both off; the reading below
+applies when a caller turns them on), in the order the pages list the knobs -- temperature, then
+top-k, then top-p:
+
+* top-k (k >= 1): keep the ids whose logit is at least the k-th largest finite logit of the row
+  (counted with multiplicity); ids with equal logits are kept or dropped together, so a tie at the
+  k-th place keeps more than k ids.  k = 0, or k at least the number of finite logits, keeps all.
+* top-p (nucleus sampling, Holtzman et al., "The Curious Case of Neural Text Degeneration",
+  ICLR 2020), 0 < p <= 1: on the distribution left by top-k (renormalised), keep the smallest set
+  of highest-probability ids whose total probability reaches p -- the ids down to the first
+  logit value at which the running total, taken over distinct values in decreasing order, is at
+  least p times the total; ties are again kept together.  p = 1 keeps all.
+* the sampled id and its confidence then come from the kept ids only, renormalised: the first id
+  (in id order) whose running weight passes u times the kept total; conf = its weight over that
+  total.
+
 Counter-based generator: Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
 numbers: as easy as 1, 2, 3", SC 2011), written from its published definition: a 4 x 32-bit
 counter and a 2 x 32-bit key; each round multiplies words 0 and 2 of the counter by the two
@@ -58,15 +74,37 @@ def row_uniform(seed: int, row: int, step: int) -> float:
     return (w0 + 0.5) / 4294967296.0
 
 
-def row_sample(row: np.ndarray, tau: float, u: float):
-    """(probability of the sampled id, sampled id) of one logit row at temperature tau; NaN and -1
-    for an invalid row (NaN or +Inf anywhere, or only -Inf)."""
+def truncation_cut(row: np.ndarray, tau: float, top_k: int = 0, top_p: float = 1.0) -> float:
+    """The smallest logit value kept by top-k and then top-p (every id whose logit is at least this
+    value is kept); -inf when neither cuts anything.  The row must be valid (see row_sample)."""
+    assert top_k >= 0 and 0.0 < top_p <= 1.0
+    x = np.asarray(row, dtype=np.float64)
+    fin = x[np.isfinite(x)]
+    cut = -np.inf
+    if 1 <= top_k < len(fin):
+        cut = float(np.sort(fin)[::-1][top_k - 1])          # the k-th largest, with multiplicity
+    if top_p < 1.0:
+        kept = fin[fin >= cut]
+        vals, counts = np.unique(kept, return_counts=True)  # distinct values, ascending
+        vals, counts = vals[::-1], counts[::-1]
+        mass = counts * np.exp((vals - vals[0]) / tau)      # weight of each distinct value's ids
+        cum = np.cumsum(mass)
+        first = int(np.flatnonzero(cum >= top_p * cum[-1])[0])
+        cut = max(cut, float(vals[first]))
+    return cut
+
+
+def row_sample(row: np.ndarray, tau: float, u: float, top_k: int = 0, top_p: float = 1.0):
+    """(probability of the sampled id, sampled id) of one logit row at temperature tau, after the
+    top-k / top-p truncation; NaN and -1 for an invalid row (NaN or +Inf anywhere, or only -Inf)."""
     x = np.asarray(row, dtype=np.float64)
     if np.isnan(x).any() or np.isposinf(x).any():
         return float("nan"), -1
     m = x.max()
     if np.isneginf(m):
         return float("nan"), -1
+    if top_k or top_p < 1.0:
+        x = np.where(x >= truncation_cut(x, tau, top_k, top_p), x, -np.inf)
     w = np.exp((x - m) / tau)
     p = w / w.sum()
     cum = np.cumsum(p)
@@ -75,7 +113,8 @@ def row_sample(row: np.ndarray, tau: float, u: float):
 
 
 def sampled_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray, blk_len: int,
-                   threshold, temperature: float, seed: int, step: int, fallback: str = C.FALLBACK_TOP1):
+                   threshold, temperature: float, seed: int, step: int, fallback: str = C.FALLBACK_TOP1,
+                   top_k: int = 0, top_p: float = 1.0):
     """One commit step with sampled predictions; same outputs as :func:`oracle.commit.confidence_commit`,
     plus ``u`` (the uniform of every row; NaN for rows not masked on entry)."""
     logits = np.asarray(logits)
@@ -86,7 +125,7 @@ def sampled_commit(logits: np.ndarray, tokens: np.ndarray, masked: np.ndarray, b
     for r in range(R):
         if masked[r]:
             us[r] = row_uniform(seed, r, step)
-            conf[r], pred[r] = row_sample(logits[r], temperature, us[r])
+            conf[r], pred[r] = row_sample(logits[r], temperature, us[r], top_k, top_p)
     out = C.decide(conf, pred, tokens, masked, blk_len, threshold, fallback)
     out["u"] = us
     return out
