@@ -340,6 +340,22 @@ def main():
         if rnd:
             sm_us.extend(t_us)
 
+    # the same step with top-k / top-p truncation (one workgroup per row, the row held in registers)
+    tr_us = {}
+    for k_, p_ in ((50, 1.0), (0, 0.9)):
+        tr_us[(k_, p_)] = []
+        for rnd in range(3):
+            for m in msk_rw:
+                m.fill_(1)
+            t_us = primed([lambda i=i: bd.bd_confidence_commit_sampled(logit_pool[i], tokens, msk_rw[i], lw.block_size,
+                                                                       T_step, temperature=1.0, seed=lw.seed,
+                                                                       step=rnd, top_k=k_, top_p=p_, conf=conf,
+                                                                       pred=pred, n_committed=ncom,
+                                                                       n_masked_left=nleft, workspace=sm_ws)
+                           for i in range(n_pool)], n_launch_us=400.0)
+            if rnd:
+                tr_us[(k_, p_)].extend(t_us)
+
     # ------------------------------- single-shot decode step / commit, 4096 prefix
     sw = W.WORKLOADS["decode_step_bf16"]
     n_copies_kv, n_copies_lg = 40, 64
@@ -476,6 +492,10 @@ def main():
                         "commit_GBps_median": round(float(np.median(com_gbs_loop)), 1),
                         "commit_rowwise_GBps_first_step": round(rw_bytes / (np.median(rw_us) * 1e-6) / 1e9, 1),
                         "commit_sampled_GBps_first_step": round(rw_bytes / (np.median(sm_us) * 1e-6) / 1e9, 1),
+                        "commit_sampled_topk50_GBps_first_step":
+                            round(rw_bytes / (np.median(tr_us[(50, 1.0)]) * 1e-6) / 1e9, 1),
+                        "commit_sampled_topp0.9_GBps_first_step":
+                            round(rw_bytes / (np.median(tr_us[(0, 0.9)]) * 1e-6) / 1e9, 1),
                         "by_threshold": loops},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),

@@ -228,10 +228,12 @@ def bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, vocab) -> int:
 
 def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold: float, temperature: float = 1.0,
                                  seed: int = 0, step: int = 0, fallback: int = BD_FALLBACK_TOP1,
-                                 vocab: Optional[int] = None, conf=None, pred=None, n_committed=None,
-                                 n_masked_left=None, want_rows: bool = True, workspace=None, stream=None):
-    """Threshold commit with sampled predictions (temperature, Philox4x32-10 keyed by seed/row/step);
-    updates ``tokens``/``masked`` in place.  Returns dict(conf, pred, n_committed, n_masked_left)."""
+                                 vocab: Optional[int] = None, top_k: int = 0, top_p: float = 1.0, conf=None,
+                                 pred=None, n_committed=None, n_masked_left=None, want_rows: bool = True,
+                                 workspace=None, stream=None):
+    """Threshold commit with sampled predictions (temperature, then top-k / top-p truncation, then
+    Philox4x32-10 keyed by seed/row/step); updates ``tokens``/``masked`` in place.  Returns
+    dict(conf, pred, n_committed, n_masked_left)."""
     rows = logits.shape[0]
     if rows % blk_len:
         raise ValueError("logits rows must be a multiple of blk_len")
@@ -249,7 +251,8 @@ def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold
     n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
     ws, nb = _workspace(bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, V), dev, workspace)
     st = lib.bd_confidence_commit_sampled(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
-                                          float(temperature), int(seed), int(step), float(threshold), int(fallback),
+                                          float(temperature), int(seed), int(step), int(top_k), float(top_p),
+                                          float(threshold), int(fallback),
                                           _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred), _ptr(n_committed),
                                           _ptr(n_masked_left), _ptr(ws), nb, _stream(stream))
     check(st, "bd_confidence_commit_sampled")

@@ -42,8 +42,8 @@ _SIGS = {
                                         _sz, _p]),
     "bd_kv_append_block": (_i, [_p, _p, _p, _p, _p, _i, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "bd_confidence_commit_sampled_workspace_size": (_sz, [_i, _i, _i]),
-    "bd_confidence_commit_sampled": (_i, [_p, _i64, _i, _i, _i, _i, _f, _u64, _u64, _f, _i, _p, _p, _p, _p, _p, _p,
-                                         _p, _sz, _p]),
+    "bd_confidence_commit_sampled": (_i, [_p, _i64, _i, _i, _i, _i, _f, _u64, _u64, _i, _f, _f, _i, _p, _p, _p, _p,
+                                         _p, _p, _p, _sz, _p]),
     "bd_lmhead_commit_workspace_size": (_sz, [_i, _i, _i]),
     "bd_lmhead_commit": (_i, [_p, _i64, _p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }

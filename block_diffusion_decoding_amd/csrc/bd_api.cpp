@@ -237,8 +237,9 @@ size_t bd_confidence_commit_sampled_workspace_size(int n_seq, int blk_len, int v
 }
 
 bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
-                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step,
-                                       float threshold, bd_fallback fallback, int32_t* tokens, uint8_t* masked,
+                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step, int top_k,
+                                       float top_p, float threshold, bd_fallback fallback, int32_t* tokens,
+                                       uint8_t* masked,
                                        float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
                                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!logits || !tokens || !masked) return BD_ERR_NULL;
@@ -247,13 +248,18 @@ bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, i
   if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
   if (std::isnan(threshold)) return BD_ERR_VALUE;
   if (!(temperature > 0.f) || std::isinf(temperature)) return BD_ERR_VALUE;
+  if (top_k < 0 || !(top_p > 0.f && top_p <= 1.f)) return BD_ERR_VALUE;
   if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
+  const bool truncate = top_k > 0 || top_p < 1.f;
+  if (truncate && vocab > bd::sample_truncated_max_vocab(dtype == BD_BF16)) return BD_ERR_UNSUPPORTED;
   const long long rows = (long long)n_seq * blk_len;
   if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
   const size_t need = bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, nullptr,
                    fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
+  if (truncate)
+    return hip_status(bd::launch_commit_sampled_truncated(a, temperature, seed, step, top_k, top_p, stream));
   return hip_status(bd::launch_commit_sampled(a, temperature, seed, step, stream));
 }
 

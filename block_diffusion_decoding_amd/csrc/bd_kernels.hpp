@@ -75,6 +75,12 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 size_t commit_sampled_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
                                  hipStream_t st);
+// Sampled predictions after top-k / top-p truncation (one workgroup per row, the
+// row held in registers: vocab at most sample_truncated_max_vocab); the
+// workspace holds the per-row confidence and id (rows * 8 bytes).
+int sample_truncated_max_vocab(int is_bf16);
+hipError_t launch_commit_sampled_truncated(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
+                                           int top_k, float top_p, hipStream_t st);
 // The decide step alone, on nchunk partials per row at `part` ([row][chunk]).
 hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st);
 

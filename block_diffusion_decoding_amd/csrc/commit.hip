@@ -21,6 +21,8 @@
 #include "commit_common.hpp"
 
 #include <algorithm>
+#include <mutex>
+#include <utility>
 
 #ifndef BD_COMMIT_TARGET_WGS
 #define BD_COMMIT_TARGET_WGS 8192
@@ -505,6 +507,542 @@ __global__ __launch_bounds__(kThreads) void sample_locate(const T* __restrict__ 
   }
 }
 
+// ---- sampling under top-k / top-p truncation ----------------------------------
+// One workgroup of 512 threads (two waves per SIMD, so that a thread has 256
+// registers) per masked row holds the whole row in registers (kTrVec 16-byte
+// vectors per thread; vector j of thread t holds ids (512 j + t) N .. + N - 1),
+// so the row is read from HBM once:
+//   1. the largest order key (a total order on the values, -0 taken as +0),
+//      the invalid flag and the count of finite values (workgroup reductions);
+//   2. the cut, the order key of the smallest kept value.  bf16 rows: counts
+//      per 16-bit key in an LDS histogram (one bin per representable value,
+//      windows of 32768 keys below the row maximum, at most two), whose running
+//      count and mass (count times the value's weight) over decreasing values
+//      place the top-k and then the top-p cut exactly, with no exponential per
+//      element.  fp32 rows: bisection over the 32-bit key, one workgroup count
+//      or mass reduction per step.
+//   3. inverse CDF over the kept ids in id order: vector totals across the
+//      workgroup give the vector holding u times the kept mass, a workgroup
+//      scan of that vector's per-thread weights the thread, and a walk of its
+//      N ids the id.  conf = weight / kept mass.
+constexpr int kTrThreads = 512;
+constexpr int kTrWaves = kTrThreads / 64;
+constexpr int kTrVec = 38;                           // 16-byte vectors per thread
+constexpr int kHistBins = 32768;                     // histogram window (keys)
+constexpr int kHistPerThread = kHistBins / kTrThreads;
+constexpr size_t kHistBytes = kHistBins * sizeof(uint32_t);
+constexpr size_t kPsBytes = (size_t)kTrVec * kTrThreads * sizeof(float);   // per-thread vector sums
+static_assert(kPsBytes <= kHistBytes, "the vector sums reuse the histogram's space");
+
+// The row is held as order keys: unsigned integers in the order of the values
+// (sign bit flipped for positive values, all bits for negative ones; -0 taken
+// as +0), so that the cut is a key and equal values share one key.
+template <typename T> struct TrElem;
+template <> struct TrElem<uint16_t> {
+  static constexpr int N = 8;
+  static constexpr uint32_t kNegInfKey = 0x007Fu;        // key of -inf
+  static constexpr uint32_t kPosInfKey = 0xFF80u;        // key of +inf (NaNs lie outside the two)
+  __device__ __forceinline__ static uint32_t key(const u32x4& r, int e) {
+    const uint32_t w = r[e >> 1];
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+  __device__ __forceinline__ static uint32_t to_key(uint32_t b) {
+    b = b == 0x8000u ? 0u : b;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+  __device__ __forceinline__ static float value_of_key(uint32_t k) { return __uint_as_float(((k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu)) << 16); }
+  __device__ __forceinline__ static uint32_t fetch(const uint16_t* p) { return *p; }
+  __device__ __forceinline__ static void put(u32x4& r, int e, uint32_t k) {
+    const uint32_t w = r[e >> 1];
+    r[e >> 1] = (e & 1) ? ((w & 0xFFFFu) | (k << 16)) : ((w & 0xFFFF0000u) | k);
+  }
+  __device__ __forceinline__ static void to_keys(u32x4& r) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) put(r, e, to_key(key(r, e)));
+  }
+};
+template <> struct TrElem<float> {
+  static constexpr int N = 4;
+  static constexpr uint32_t kNegInfKey = 0x007FFFFFu;
+  static constexpr uint32_t kPosInfKey = 0xFF800000u;
+  __device__ __forceinline__ static uint32_t key(const u32x4& r, int e) { return r[e]; }
+  __device__ __forceinline__ static uint32_t to_key(uint32_t b) {
+    b = b == 0x80000000u ? 0u : b;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  __device__ __forceinline__ static float value_of_key(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+  __device__ __forceinline__ static uint32_t fetch(const float* p) { return __float_as_uint(*p); }
+  __device__ __forceinline__ static void put(u32x4& r, int e, uint32_t k) { r[e] = k; }
+  __device__ __forceinline__ static void to_keys(u32x4& r) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) r[e] = to_key(r[e]);
+  }
+};
+
+// Opaque to the optimiser, placed before the work on each vector of every
+// pass: a pass recomputes what it needs from the keys instead of keeping
+// per-element values alive from an earlier pass, and the vectors of a pass
+// are processed in turn rather than all interleaved (either would spill).
+__device__ __forceinline__ void tr_fence(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// r[j] for a workgroup-uniform j, by selects (no indexed register access).
+__device__ __forceinline__ u32x4 tr_pick(const u32x4 (&r)[kTrVec], int j) {
+  u32x4 v = r[0];
+#pragma unroll
+  for (int i = 1; i < kTrVec; ++i) {
+    const bool h = i == j;
+    v.x = h ? r[i].x : v.x;
+    v.y = h ? r[i].y : v.y;
+    v.z = h ? r[i].z : v.z;
+    v.w = h ? r[i].w : v.w;
+  }
+  return v;
+}
+
+struct TrShared {
+  float redf[kTrWaves];
+  uint32_t redu[kTrWaves];
+  float vtot[kTrVec];
+  uint32_t cut_off;              // offset (below the largest key) of the smallest kept value
+  float cut_mass;                // running mass through that value
+  int first_thr, last_id, id;
+};
+
+// Workgroup-uniform values (read from LDS) moved to scalar registers, so that
+// branches on them are scalar branches.
+__device__ __forceinline__ uint32_t tr_uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float tr_uni(float v) { return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v))); }
+__device__ __forceinline__ int tr_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Workgroup sums (every thread gets the same total; fixed order).
+__device__ __forceinline__ float tr_sum(float v, TrShared& sh, int lane, int wave) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) sh.redf[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kTrWaves; ++w) t += sh.redf[w];
+  return tr_uni(t);
+}
+__device__ __forceinline__ uint32_t tr_sum(uint32_t v, TrShared& sh, int lane, int wave) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  __syncthreads();
+  if (lane == 0) sh.redu[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kTrWaves; ++w) t += sh.redu[w];
+  return tr_uni(t);
+}
+__device__ __forceinline__ uint32_t tr_max(uint32_t v, TrShared& sh, int lane, int wave) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor(v, m, 64));
+  __syncthreads();
+  if (lane == 0) sh.redu[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kTrWaves; ++w) t = max(t, sh.redu[w]);
+  return tr_uni(t);
+}
+
+// Exclusive workgroup scan in thread order: c (exact) and m (fp32, fixed order).
+__device__ __forceinline__ void tr_scan(uint32_t c, float m, uint32_t& c_ex, float& m_ex, uint32_t& c_tot,
+                                        float& m_tot, TrShared& sh, int lane, int wave) {
+  uint32_t ci = c;
+  float mi = m;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t yc = __shfl_up(ci, off, 64);
+    const float ym = __shfl_up(mi, off, 64);
+    if (lane >= off) {
+      ci += yc;
+      mi += ym;
+    }
+  }
+  uint32_t cx = __shfl_up(ci, 1, 64);
+  float mx = __shfl_up(mi, 1, 64);
+  if (lane == 0) {
+    cx = 0;
+    mx = 0.f;
+  }
+  __syncthreads();
+  if (lane == 63) {
+    sh.redu[wave] = ci;
+    sh.redf[wave] = mi;
+  }
+  __syncthreads();
+  uint32_t cb = 0, ct = 0;
+  float mb = 0.f, mt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kTrWaves; ++w) {
+    if (w < wave) {
+      cb += sh.redu[w];
+      mb += sh.redf[w];
+    }
+    ct += sh.redu[w];
+    mt += sh.redf[w];
+  }
+  c_ex = cb + cx;
+  m_ex = mb + mx;
+  c_tot = tr_uni(ct);
+  m_tot = tr_uni(mt);
+}
+
+template <typename T, bool kVector>
+__global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restrict__ logits, int64_t row_stride,
+                                                               int vocab, const uint8_t* __restrict__ masked,
+                                                               float c, int top_k, float top_p, uint32_t seed_lo,
+                                                               uint32_t seed_hi, uint32_t step_lo, uint32_t step_hi,
+                                                               float* __restrict__ row_conf,
+                                                               int32_t* __restrict__ row_pred) {
+  using E = TrElem<T>;
+  constexpr int N = E::N;
+  constexpr bool kHist = sizeof(T) == 2;
+  extern __shared__ __attribute__((aligned(16))) uint32_t hist[];
+  __shared__ TrShared sh;
+  const int row = blockIdx.x;
+  if (!masked[row]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T* base = logits + (int64_t)row * row_stride;
+
+  // ---- the row into registers: every whole vector first (clamped addresses,
+  // no branch between the loads), then the ragged or missing ones by element
+  u32x4 r[kTrVec];
+  if (kVector) {
+    const int last_full = (vocab / N - 1) * N;   // vocab >= N on this path
+#pragma unroll
+    for (int j = 0; j < kTrVec; ++j) {
+      const int v0 = min((j * kTrThreads + tid) * N, last_full);
+      r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + v0));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kTrVec; ++j) {
+    const int v0 = (j * kTrThreads + tid) * N;
+    if (!kVector || v0 + N > vocab) {
+      // ids past the row hold -inf's key (never kept)
+#pragma unroll
+      for (int e = 0; e < N; ++e) E::put(r[j], e, v0 + e < vocab ? E::to_key(E::fetch(base + v0 + e)) : E::kNegInfKey);
+    } else {
+      E::to_keys(r[j]);
+    }
+  }
+
+  // ---- 1. largest key, invalid flag (a NaN or +inf), finite count
+  uint32_t kmax = 0, nfin = 0, bad = 0;
+#pragma unroll
+  for (int j = 0; j < kTrVec; ++j) {
+    tr_fence(r[j]);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const uint32_t k = E::key(r[j], e);
+      const bool fin = k > E::kNegInfKey && k < E::kPosInfKey;
+      bad |= k >= E::kPosInfKey || k < E::kNegInfKey;
+      nfin += fin;
+      kmax = fin ? max(kmax, k) : kmax;
+    }
+  }
+  bad = tr_max(bad, sh, lane, wave);
+  nfin = tr_sum(nfin, sh, lane, wave);
+  kmax = tr_max(kmax, sh, lane, wave);
+  if (bad || nfin == 0) {
+    if (tid == 0) {
+      row_conf[row] = __builtin_nanf("");
+      row_pred[row] = -1;
+    }
+    return;
+  }
+  const float M = E::value_of_key(kmax), mb = M * c;
+  auto weight = [&](float x) __attribute__((always_inline)) { return exp2_fast(__builtin_fmaf(x, c, -mb)); };
+  const bool need_k = top_k >= 1 && (uint32_t)top_k < nfin;
+  const bool need_p = top_p < 1.f;
+
+  // ---- 2. the cut
+  uint32_t cut_key = E::kNegInfKey + 1;   // keep every finite value
+  if constexpr (kHist) {
+    // bins of window w: offsets kmax - key - 32768 w in [0, 32768)
+    auto build = [&](uint32_t wbase) __attribute__((always_inline)) {
+      uint4* h4 = reinterpret_cast<uint4*>(hist);
+      for (int i = tid; i < kHistBins / 4; i += kTrThreads) h4[i] = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kTrVec; ++j) {
+        tr_fence(r[j]);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const uint32_t k = E::key(r[j], e);
+          const uint32_t off = kmax - k - wbase;
+          if (k > E::kNegInfKey && off < (uint32_t)kHistBins) atomicAdd(&hist[off], 1u);
+        }
+      }
+      __syncthreads();
+    };
+    // mass of bin i of this thread's 32 (count times the weight of its value), kept
+    // out of fused multiply-adds so that the scan and the walk below round alike
+    auto bin_mass = [&](uint32_t wbase, int i, uint32_t cnt) __attribute__((always_inline)) {
+      if (cnt == 0) return 0.f;
+      const uint32_t off = wbase + (uint32_t)(tid * kHistPerThread + i);
+      return __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
+    };
+    uint32_t c_ex = 0, own_c = 0, c_tot = 0;
+    float m_ex = 0.f, own_m = 0.f, m_tot = 0.f;
+    auto scan = [&](uint32_t wbase, uint32_t cbase, float mbase) __attribute__((always_inline)) {
+      own_c = 0;
+      own_m = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < kHistPerThread; ++i) {
+        const uint32_t cnt = hist[tid * kHistPerThread + i];
+        own_c += cnt;
+        own_m = __fadd_rn(own_m, bin_mass(wbase, i, cnt));
+      }
+      tr_scan(own_c, own_m, c_ex, m_ex, c_tot, m_tot, sh, lane, wave);
+      c_ex += cbase;
+      m_ex = __fadd_rn(mbase, m_ex);
+      c_tot += cbase;
+      m_tot = __fadd_rn(mbase, m_tot);
+    };
+    // The first bin whose running count reaches k (exact: one thread brackets it).
+    auto find_count = [&](uint32_t wbase, uint32_t k) __attribute__((always_inline)) {
+      if (c_ex < k && k <= c_ex + own_c) {
+        uint32_t cc = c_ex;
+        float lm = 0.f;
+        for (int i = 0; i < kHistPerThread; ++i) {
+          const uint32_t cnt = hist[tid * kHistPerThread + i];
+          cc += cnt;
+          lm = __fadd_rn(lm, bin_mass(wbase, i, cnt));
+          if (cc >= k) {
+            sh.cut_off = wbase + (uint32_t)(tid * kHistPerThread + i);
+            sh.cut_mass = __fadd_rn(m_ex, lm);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+    };
+    // The first bin whose running mass reaches the target: the first thread whose
+    // running mass through its last bin does, then its bins in order (the last
+    // one reaches it, as the sums are formed alike).  None: keep the window.
+    auto find_mass = [&](uint32_t wbase, float target) __attribute__((always_inline)) {
+      if (tid == 0) sh.first_thr = kTrThreads;
+      __syncthreads();
+      if (__fadd_rn(m_ex, own_m) >= target) atomicMin(&sh.first_thr, tid);
+      __syncthreads();
+      if (tid == sh.first_thr) {
+        float lm = 0.f;
+        for (int i = 0; i < kHistPerThread; ++i) {
+          lm = __fadd_rn(lm, bin_mass(wbase, i, hist[tid * kHistPerThread + i]));
+          if (__fadd_rn(m_ex, lm) >= target) {
+            sh.cut_off = wbase + (uint32_t)(tid * kHistPerThread + i);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+    };
+    // Windows are built one at a time, window 0 first (the largest values):
+    // top-k needs the window holding the k-th largest value; top-p needs the
+    // top-k mass (or, with top-k off, the total over both windows) and then the
+    // window holding its crossing.  At most three builds.
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
+    uint32_t off_k = kNone, off_p = kNone, tc0 = 0;
+    float tm0 = 0.f, zk = 0.f;
+    bool k_done = !need_k, z_known = need_k ? false : !need_p, p_done = !need_p;
+    int want = 0;
+#pragma unroll 1
+    for (int it = 0; it < 4 && want >= 0; ++it) {
+      const uint32_t wbase = want ? (uint32_t)kHistBins : 0u;
+      build(wbase);
+      scan(wbase, want ? tc0 : 0u, want ? tm0 : 0.f);
+      if (want == 0) {
+        tc0 = c_tot;
+        tm0 = m_tot;
+      }
+      int next = -1;
+      if (!k_done) {
+        if ((uint32_t)top_k <= c_tot) {
+          if (tid == 0) sh.cut_off = kNone;
+          __syncthreads();
+          find_count(wbase, (uint32_t)top_k);
+          off_k = tr_uni(sh.cut_off);
+          zk = tr_uni(sh.cut_mass);
+          k_done = z_known = true;
+        } else {
+          next = 1;
+        }
+      } else if (!z_known) {
+        if (want == 0 && nfin > c_tot) {
+          next = 1;
+        } else {
+          zk = m_tot;
+          z_known = true;
+        }
+      }
+      if (next < 0 && !p_done) {
+        const float target = top_p * zk;
+        const int wp = (target <= tm0 || nfin == tc0) ? 0 : 1;
+        if (wp == want) {
+          if (tid == 0) sh.cut_off = kNone;
+          __syncthreads();
+          find_mass(wbase, target);
+          off_p = tr_uni(sh.cut_off);
+          p_done = true;
+        } else {
+          next = wp;
+        }
+      }
+      want = next;
+    }
+    const uint32_t cut_off = min(off_k, off_p);
+    if (cut_off != kNone) cut_key = kmax - cut_off;
+  } else {
+    // bisection over the order key: the largest key t with count (mass) of the
+    // values at or above t reaching k (the top-p target)
+    // (t is always above -inf's key)
+    auto count_ge = [&](uint32_t t) __attribute__((always_inline)) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int j = 0; j < kTrVec; ++j) {
+        tr_fence(r[j]);
+#pragma unroll
+        for (int e = 0; e < N; ++e) n += E::key(r[j], e) >= t;
+      }
+      return tr_sum(n, sh, lane, wave);
+    };
+    auto mass_ge = [&](uint32_t t) __attribute__((always_inline)) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTrVec; ++j) {
+        tr_fence(r[j]);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const uint32_t k = E::key(r[j], e);
+          s += k >= t ? weight(E::value_of_key(k)) : 0.f;
+        }
+        asm volatile("" : "+v"(s));
+      }
+      return tr_sum(s, sh, lane, wave);
+    };
+    uint32_t lo = E::kNegInfKey + 1;
+    if (need_k) {
+      uint32_t hi = kmax;
+      while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo + 1) / 2;
+        if (count_ge(mid) >= (uint32_t)top_k) lo = mid;
+        else hi = mid - 1;
+      }
+    }
+    if (need_p) {
+      const float target = top_p * mass_ge(lo);
+      uint32_t hi = kmax;
+      while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo + 1) / 2;
+        if (mass_ge(mid) >= target) lo = mid;
+        else hi = mid - 1;
+      }
+    }
+    cut_key = lo;
+  }
+
+  // ---- 3. inverse CDF over the kept ids, in id order.  Each thread's kept
+  // weight per vector goes to LDS (the histogram's space), ps[j][t].
+  auto kept_w = [&](uint32_t k) __attribute__((always_inline)) {
+    return k >= cut_key ? weight(E::value_of_key(k)) : 0.f;
+  };
+  float* ps = reinterpret_cast<float*>(hist);
+  __syncthreads();   // the histogram is no longer read
+#pragma unroll
+  for (int j = 0; j < kTrVec; ++j) {
+    tr_fence(r[j]);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) s += kept_w(E::key(r[j], e));
+    asm volatile("" ::"v"(s));
+    ps[j * kTrThreads + tid] = s;
+  }
+  if (tid == 0) {
+    sh.last_id = -1;
+    sh.first_thr = kTrThreads;
+    sh.id = -1;
+  }
+  __syncthreads();
+  // vector totals: wave w adds vectors w, w + 8, ... (eight consecutive threads' sums per lane)
+  for (int j = wave; j < kTrVec; j += kTrWaves) {
+    const float* q = ps + j * kTrThreads + lane * (kTrThreads / 64);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kTrThreads / 64; ++i) t += q[i];
+    t = wave_sum(t);
+    if (lane == 0) sh.vtot[j] = t;
+  }
+  __syncthreads();
+  float Z = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTrVec; ++j) Z += sh.vtot[j];
+  Z = tr_uni(Z);
+  const uint32_t wu = philox_word0((uint32_t)row, step_lo, step_hi, 0u, seed_lo, seed_hi);
+  const float target = (float)(((double)wu + 0.5) * (1.0 / 4294967296.0)) * Z;
+  int js = -1;
+  float before = 0.f;
+  for (int j = 0; j < kTrVec; ++j) {
+    const float t = tr_uni(sh.vtot[j]);
+    if (before + t > target) {
+      js = j;
+      break;
+    }
+    before += t;
+  }
+  // the first thread of vector js whose running weight passes the target
+  const float sj = js >= 0 ? ps[js * kTrThreads + tid] : 0.f;
+  const float res = target - before;
+  float pre = 0.f;
+  {
+    uint32_t cdummy, ctot;
+    float mtot;
+    tr_scan(0u, sj, cdummy, pre, ctot, mtot, sh, lane, wave);
+  }
+  if (js >= 0 && pre + sj > res) atomicMin(&sh.first_thr, tid);
+  __syncthreads();
+  if (js >= 0 && tid == sh.first_thr) {
+    // its ids in order: the running weight is formed as in sj, so the last one passes
+    const u32x4 v = tr_pick(r, js);
+    float lw = 0.f;
+    int hit = -1;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      lw += kept_w(E::key(v, e));
+      if (hit < 0 && pre + lw > res) hit = (js * kTrThreads + tid) * N + e;
+    }
+    sh.id = hit;
+  }
+  __syncthreads();
+  if (tr_uni(sh.id) < 0) {
+    // rounding left no vector or thread past the target: the last kept id
+    int last = -1;
+#pragma unroll
+    for (int j = 0; j < kTrVec; ++j) {
+      tr_fence(r[j]);
+#pragma unroll
+      for (int e = 0; e < N; ++e) last = E::key(r[j], e) >= cut_key ? (j * kTrThreads + tid) * N + e : last;
+    }
+    atomicMax(&sh.last_id, last);
+    __syncthreads();
+  }
+  const int id = tr_uni(sh.id >= 0 ? sh.id : sh.last_id);
+  if (tid == ((id / N) & (kTrThreads - 1))) {
+    const u32x4 v = tr_pick(r, id / N / kTrThreads);
+    const int ee = id % N;
+    float w = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (e == ee) w = kept_w(E::key(v, e));
+    row_pred[row] = id;
+    row_conf[row] = w / Z;
+  }
+}
+
 hipError_t launch_decide(const void* part, int nchunk, const float* row_conf, const int32_t* row_pred,
                          const CommitArgs& a, hipStream_t st) {
   // Rows with many partials (the fused projection: one per workgroup) get 32 threads each.
@@ -563,6 +1101,46 @@ hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decide(part, nchunk, row_conf, row_pred, a, st);
+}
+
+int sample_truncated_max_vocab(int is_bf16) { return kTrVec * kTrThreads * (is_bf16 ? 8 : 4); }
+
+hipError_t launch_commit_sampled_truncated(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
+                                           int top_k, float top_p, hipStream_t st) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    const std::pair<const void*, size_t> fs[] = {
+        {reinterpret_cast<const void*>(&sample_truncated<uint16_t, true>), kHistBytes},
+        {reinterpret_cast<const void*>(&sample_truncated<uint16_t, false>), kHistBytes},
+        {reinterpret_cast<const void*>(&sample_truncated<float, true>), kPsBytes},
+        {reinterpret_cast<const void*>(&sample_truncated<float, false>), kPsBytes}};
+    for (const auto& f : fs) {
+      const hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.second);
+      if (e != hipSuccess) attr_err = e;
+    }
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  const int64_t rows = (int64_t)a.n_seq * a.blk_len;
+  float* row_conf = reinterpret_cast<float*>(a.ws);
+  int32_t* row_pred = reinterpret_cast<int32_t*>(row_conf + rows);
+  const float c = kLog2e / temperature;
+  const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32), tl = (uint32_t)step, th = (uint32_t)(step >> 32);
+  const int elem = a.is_bf16 ? 2 : 4;
+  const bool vec = ((uintptr_t)a.logits % 16 == 0) && ((a.row_stride * elem) % 16 == 0) && a.vocab >= 16 / elem;
+  const dim3 grid((unsigned)rows), block(kTrThreads);
+  if (a.is_bf16) {
+    const uint16_t* lg = reinterpret_cast<const uint16_t*>(a.logits);
+    if (vec) hipLaunchKernelGGL((sample_truncated<uint16_t, true>), grid, block, kHistBytes, st, lg, a.row_stride, a.vocab, a.masked, c, top_k, top_p, sl, sh, tl, th, row_conf, row_pred);
+    else hipLaunchKernelGGL((sample_truncated<uint16_t, false>), grid, block, kHistBytes, st, lg, a.row_stride, a.vocab, a.masked, c, top_k, top_p, sl, sh, tl, th, row_conf, row_pred);
+  } else {
+    const float* lg = reinterpret_cast<const float*>(a.logits);
+    if (vec) hipLaunchKernelGGL((sample_truncated<float, true>), grid, block, kPsBytes, st, lg, a.row_stride, a.vocab, a.masked, c, top_k, top_p, sl, sh, tl, th, row_conf, row_pred);
+    else hipLaunchKernelGGL((sample_truncated<float, false>), grid, block, kPsBytes, st, lg, a.row_stride, a.vocab, a.masked, c, top_k, top_p, sl, sh, tl, th, row_conf, row_pred);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decide(nullptr, 1, row_conf, row_pred, a, st);
 }
 
 int commit_chunks_per_row(long long rows, int vocab) {

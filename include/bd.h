@@ -240,27 +240,37 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
  * from the full softmax with no truncation.  bd_confidence_commit takes the
  * argmax; this call samples:
  *
- *   p_v = softmax(logits[r] / temperature)_v over the whole vocabulary;
+ *   p_v = softmax(logits[r] / temperature)_v over the ids that the truncation
+ *         keeps (all of them for top_k = 0, top_p = 1, as on the pages);
  *   u   = (w + 1/2) / 2^32, w = word 0 of Philox4x32-10 (Salmon et al., SC
  *         2011) of counter (r, step mod 2^32, step >> 32, 0) under key
  *         (seed mod 2^32, seed >> 32);
- *   pred[r] = the first id v whose cumulative probability sum_{w<=v} p_w
+ *   pred[r] = the first kept id v whose cumulative probability sum_{w<=v} p_w
  *         exceeds u (inverse-CDF sampling in id order);
- *   conf[r] = p_pred.
+ *   conf[r] = p_pred (renormalised over the kept ids).
+ * Truncation, after the temperature: top_k >= 1 keeps the ids whose logit is
+ * at least the top_k-th largest finite logit (ties kept together; 0 = off);
+ * then top_p in (0, 1] keeps, of those, the ids down to the first logit value
+ * (in decreasing order) at which their renormalised probability reaches top_p
+ * (nucleus sampling, Holtzman et al., ICLR 2020; ties kept together; 1 = off).
  * Then the threshold rule, the fallback and the state update of
  * bd_confidence_commit.  Invalid rows as there (conf NaN, pred -1).
- *   temperature > 0 and finite (BD_ERR_VALUE otherwise); a new `step` per
- *   denoising step gives fresh draws; the same (seed, step) repeats them.
+ *   temperature > 0 and finite, top_k >= 0, 0 < top_p <= 1 (BD_ERR_VALUE
+ *   otherwise); a new `step` per denoising step gives fresh draws; the same
+ *   (seed, step) repeats them.
+ *   With truncation on, vocab is at most 155648 (bf16) or 77824 (fp32)
+ *   (BD_ERR_UNSUPPORTED otherwise): one workgroup holds a row in registers.
  *   workspace of bd_confidence_commit_sampled_workspace_size() bytes;
  *   contents on entry are ignored.  Other arguments as bd_confidence_commit.
- * The id is found by rescanning, for each masked row, only the vocabulary
- * chunk in which the running sum passes u (one extra read of 1/k of the row
- * for k chunks per row).
+ * Without truncation the id is found by rescanning, for each masked row, only
+ * the vocabulary chunk in which the running sum passes u (one extra read of
+ * 1/k of the row for k chunks per row); with it, each row is read once.
  * ---------------------------------------------------------------------- */
 size_t bd_confidence_commit_sampled_workspace_size(int n_seq, int blk_len, int vocab);
 bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
-                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step,
-                                       float threshold, bd_fallback fallback, int32_t* tokens, uint8_t* masked,
+                                       bd_dtype dtype, float temperature, uint64_t seed, uint64_t step, int top_k,
+                                       float top_p, float threshold, bd_fallback fallback, int32_t* tokens,
+                                       uint8_t* masked,
                                        float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
                                        void* workspace, size_t ws_bytes, hipStream_t stream);
 

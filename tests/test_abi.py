@@ -138,12 +138,12 @@ def test_sampled_commit_validation():
     assert ws >= L.lib.bd_confidence_commit_workspace_size(2, 32, 151936) + 64 * 8   # finer chunks, + (conf, id)
 
     def call(**kw):
-        a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, tau=1.0, seed=5, step=0, thr=0.95,
-                 fb=1, tok=FAKE, msk=FAKE, ws=FAKE, nb=ws)
+        a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, tau=1.0, seed=5, step=0, k=0, p=1.0,
+                 thr=0.95, fb=1, tok=FAKE, msk=FAKE, ws=FAKE, nb=ws)
         a.update(kw)
         return L.lib.bd_confidence_commit_sampled(a["lg"], a["stride"], a["n"], a["T"], a["V"], a["dt"], a["tau"],
-                                                  a["seed"], a["step"], a["thr"], a["fb"], a["tok"], a["msk"], None,
-                                                  None, None, None, a["ws"], a["nb"], None)
+                                                  a["seed"], a["step"], a["k"], a["p"], a["thr"], a["fb"], a["tok"],
+                                                  a["msk"], None, None, None, None, a["ws"], a["nb"], None)
     assert call(lg=None) == L.BD_ERR_NULL
     assert call(stride=100) == L.BD_ERR_SHAPE
     assert call(tau=0.0) == L.BD_ERR_VALUE
@@ -153,6 +153,18 @@ def test_sampled_commit_validation():
     assert call(thr=math.nan) == L.BD_ERR_VALUE
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
     assert call(seed=2**64 - 1, step=2**63, nb=0) == L.BD_ERR_WORKSPACE    # 64-bit arguments pass through
+    # truncation: top_k >= 0, 0 < top_p <= 1; rows held in registers bound the vocabulary
+    assert call(k=-1) == L.BD_ERR_VALUE
+    assert call(p=0.0) == L.BD_ERR_VALUE
+    assert call(p=1.5) == L.BD_ERR_VALUE
+    assert call(p=math.nan) == L.BD_ERR_VALUE
+    assert call(k=50, nb=0) == L.BD_ERR_WORKSPACE and call(p=0.9, nb=0) == L.BD_ERR_WORKSPACE
+    big = L.lib.bd_confidence_commit_sampled_workspace_size(2, 32, 155649)
+    assert call(V=155649, stride=155656, k=50, nb=big) == L.BD_ERR_UNSUPPORTED
+    assert call(V=155649, stride=155656, nb=0) == L.BD_ERR_WORKSPACE       # no truncation: any vocabulary
+    f32 = L.lib.bd_confidence_commit_sampled_workspace_size(2, 32, 77825)
+    assert call(V=77825, stride=77828, dt=L.BD_F32, p=0.5, nb=f32) == L.BD_ERR_UNSUPPORTED
+    assert call(V=77824, stride=77824, dt=L.BD_F32, p=0.5, nb=0) == L.BD_ERR_WORKSPACE
 
 
 def test_paged_validation():
