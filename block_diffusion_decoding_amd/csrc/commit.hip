@@ -530,13 +530,20 @@ constexpr int kTrWaves = kTrThreads / 64;
 constexpr int kTrVec = 38;                           // 16-byte vectors per thread
 constexpr int kHistBins = 32768;                     // histogram window (keys)
 constexpr int kHistPerThread = kHistBins / kTrThreads;
-constexpr size_t kHistBytes = kHistBins * sizeof(uint32_t);
+// One pad word after every 64 bins: the 64 bins a thread scans start 65 words
+// after its neighbour's, so a wave's scan reads fall in distinct banks.
+constexpr int kHistWords = kHistBins + kHistBins / 64;
+constexpr size_t kHistBytes = kHistWords * sizeof(uint32_t);
+static_assert(kHistPerThread == 64, "one pad word per thread's bins");
+__device__ __forceinline__ uint32_t hist_at(uint32_t off) { return off + (off >> 6); }
 constexpr size_t kPsBytes = (size_t)kTrVec * kTrThreads * sizeof(float);   // per-thread vector sums
 static_assert(kPsBytes <= kHistBytes, "the vector sums reuse the histogram's space");
 
 // The row is held as order keys: unsigned integers in the order of the values
 // (sign bit flipped for positive values, all bits for negative ones; -0 taken
 // as +0), so that the cut is a key and equal values share one key.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 template <typename T> struct TrElem;
 template <> struct TrElem<uint16_t> {
   static constexpr int N = 8;
@@ -556,9 +563,40 @@ template <> struct TrElem<uint16_t> {
     const uint32_t w = r[e >> 1];
     r[e >> 1] = (e & 1) ? ((w & 0xFFFFu) | (k << 16)) : ((w & 0xFFFF0000u) | k);
   }
+  // Both halves of each word at once (packed 16-bit integer operations):
+  // flip the sign bit of positive values and every bit of negative ones, then
+  // move -0 (key 0x7FFF) up to +0's key.
   __device__ __forceinline__ static void to_keys(u32x4& r) {
 #pragma unroll
-    for (int e = 0; e < N; ++e) put(r, e, to_key(key(r, e)));
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = r[i];
+      const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (short)15);
+      const uint32_t k = w ^ (neg | 0x80008000u);
+      const u16x2 nz = __builtin_elementwise_min(__builtin_bit_cast(u16x2, k ^ 0x7FFF7FFFu), u16x2{1, 1});
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, k) + (u16x2{1, 1} - nz));
+    }
+  }
+  // Largest and smallest key and the count of keys above -inf's, for both
+  // halves at once (count halves hold at most 4 kTrVec).  (The elements are
+  // copied out before the bit casts: a bit cast of a vector element in place
+  // reads element 0 with this compiler.)
+  __device__ __forceinline__ static void scan_keys(const u32x4& r, u16x2& kmax, u16x2& kmin, u16x2& nfin) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = r[i];
+      const u16x2 k = __builtin_bit_cast(u16x2, w);
+      kmax = __builtin_elementwise_max(kmax, k);
+      kmin = __builtin_elementwise_min(kmin, k);
+      nfin += __builtin_elementwise_min(k - u16x2{(unsigned short)kNegInfKey, (unsigned short)kNegInfKey}, u16x2{1, 1});
+    }
+  }
+  // Largest key of the vector.
+  __device__ __forceinline__ static uint32_t vmax(const u32x4& r) {
+    const uint32_t w0 = r[0], w1 = r[1], w2 = r[2], w3 = r[3];
+    const u16x2 m = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, w0), __builtin_bit_cast(u16x2, w1)),
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, w2), __builtin_bit_cast(u16x2, w3)));
+    return max((uint32_t)m.x, (uint32_t)m.y);
   }
 };
 template <> struct TrElem<float> {
@@ -577,6 +615,7 @@ template <> struct TrElem<float> {
 #pragma unroll
     for (int e = 0; e < N; ++e) r[e] = to_key(r[e]);
   }
+  __device__ __forceinline__ static uint32_t vmax(const u32x4& r) { return max(max(r[0], r[1]), max(r[2], r[3])); }
 };
 
 // Opaque to the optimiser, placed before the work on each vector of every
@@ -733,16 +772,30 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
 
   // ---- 1. largest key, invalid flag (a NaN or +inf), finite count
   uint32_t kmax = 0, nfin = 0, bad = 0;
+  if constexpr (kHist) {
+    // a valid row has no key above +inf's or below -inf's; then the largest key
+    // is the largest finite one unless every value is -inf (no finite count)
+    u16x2 mx{0, 0}, mn{0xFFFF, 0xFFFF}, nf{0, 0};
 #pragma unroll
-  for (int j = 0; j < kTrVec; ++j) {
-    tr_fence(r[j]);
+    for (int j = 0; j < kTrVec; ++j) {
+      tr_fence(r[j]);
+      E::scan_keys(r[j], mx, mn, nf);
+    }
+    kmax = max((uint32_t)mx.x, (uint32_t)mx.y);
+    bad = kmax >= E::kPosInfKey || min((uint32_t)mn.x, (uint32_t)mn.y) < E::kNegInfKey;
+    nfin = (uint32_t)nf.x + (uint32_t)nf.y;
+  } else {
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
-      const uint32_t k = E::key(r[j], e);
-      const bool fin = k > E::kNegInfKey && k < E::kPosInfKey;
-      bad |= k >= E::kPosInfKey || k < E::kNegInfKey;
-      nfin += fin;
-      kmax = fin ? max(kmax, k) : kmax;
+    for (int j = 0; j < kTrVec; ++j) {
+      tr_fence(r[j]);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const uint32_t k = E::key(r[j], e);
+        const bool fin = k > E::kNegInfKey && k < E::kPosInfKey;
+        bad |= k >= E::kPosInfKey || k < E::kNegInfKey;
+        nfin += fin;
+        kmax = fin ? max(kmax, k) : kmax;
+      }
     }
   }
   bad = tr_max(bad, sh, lane, wave);
@@ -764,10 +817,13 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
   uint32_t cut_key = E::kNegInfKey + 1;   // keep every finite value
   if constexpr (kHist) {
     // bins of window w: offsets kmax - key - 32768 w in [0, 32768)
-    auto build = [&](uint32_t wbase) __attribute__((always_inline)) {
+    // With `rest`, also the mass of the finite values below the window (the
+    // total mass then needs no second window).
+    auto build = [&](uint32_t wbase, bool rest) __attribute__((always_inline)) {
       uint4* h4 = reinterpret_cast<uint4*>(hist);
-      for (int i = tid; i < kHistBins / 4; i += kTrThreads) h4[i] = make_uint4(0, 0, 0, 0);
+      for (int i = tid; i < kHistWords / 4; i += kTrThreads) h4[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
+      float rm = 0.f;
 #pragma unroll
       for (int j = 0; j < kTrVec; ++j) {
         tr_fence(r[j]);
@@ -775,16 +831,18 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
         for (int e = 0; e < N; ++e) {
           const uint32_t k = E::key(r[j], e);
           const uint32_t off = kmax - k - wbase;
-          if (k > E::kNegInfKey && off < (uint32_t)kHistBins) atomicAdd(&hist[off], 1u);
+          if (k > E::kNegInfKey && off < (uint32_t)kHistBins) atomicAdd(&hist[hist_at(off)], 1u);
+          if (rest && k > E::kNegInfKey && off >= (uint32_t)kHistBins) rm += weight(E::value_of_key(k));
         }
+        if (rest) asm volatile("" : "+v"(rm));
       }
-      __syncthreads();
+      return rest ? tr_sum(rm, sh, lane, wave) : (__syncthreads(), 0.f);
     };
     // mass of bin i of this thread's 32 (count times the weight of its value), kept
     // out of fused multiply-adds so that the scan and the walk below round alike
     auto bin_mass = [&](uint32_t wbase, int i, uint32_t cnt) __attribute__((always_inline)) {
       if (cnt == 0) return 0.f;
-      const uint32_t off = wbase + (uint32_t)(tid * kHistPerThread + i);
+      const uint32_t off = wbase + (uint32_t)(tid * kHistPerThread + i);   // bin offset below the maximum
       return __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
     };
     uint32_t c_ex = 0, own_c = 0, c_tot = 0;
@@ -794,7 +852,7 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
       own_m = 0.f;
 #pragma unroll 8
       for (int i = 0; i < kHistPerThread; ++i) {
-        const uint32_t cnt = hist[tid * kHistPerThread + i];
+        const uint32_t cnt = hist[tid * (kHistPerThread + 1) + i];
         own_c += cnt;
         own_m = __fadd_rn(own_m, bin_mass(wbase, i, cnt));
       }
@@ -810,7 +868,7 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
         uint32_t cc = c_ex;
         float lm = 0.f;
         for (int i = 0; i < kHistPerThread; ++i) {
-          const uint32_t cnt = hist[tid * kHistPerThread + i];
+          const uint32_t cnt = hist[tid * (kHistPerThread + 1) + i];
           cc += cnt;
           lm = __fadd_rn(lm, bin_mass(wbase, i, cnt));
           if (cc >= k) {
@@ -833,7 +891,7 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
       if (tid == sh.first_thr) {
         float lm = 0.f;
         for (int i = 0; i < kHistPerThread; ++i) {
-          lm = __fadd_rn(lm, bin_mass(wbase, i, hist[tid * kHistPerThread + i]));
+          lm = __fadd_rn(lm, bin_mass(wbase, i, hist[tid * (kHistPerThread + 1) + i]));
           if (__fadd_rn(m_ex, lm) >= target) {
             sh.cut_off = wbase + (uint32_t)(tid * kHistPerThread + i);
             break;
@@ -850,15 +908,18 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
     uint32_t off_k = kNone, off_p = kNone, tc0 = 0;
     float tm0 = 0.f, zk = 0.f;
     bool k_done = !need_k, z_known = need_k ? false : !need_p, p_done = !need_p;
+    const bool want_rest = !need_k && need_p;   // the total mass from window 0's build
+    float rest_m = 0.f;
     int want = 0;
 #pragma unroll 1
     for (int it = 0; it < 4 && want >= 0; ++it) {
       const uint32_t wbase = want ? (uint32_t)kHistBins : 0u;
-      build(wbase);
+      const float rm = build(wbase, want_rest && want == 0);
       scan(wbase, want ? tc0 : 0u, want ? tm0 : 0.f);
       if (want == 0) {
         tc0 = c_tot;
         tm0 = m_tot;
+        rest_m = rm;
       }
       int next = -1;
       if (!k_done) {
@@ -873,12 +934,8 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
           next = 1;
         }
       } else if (!z_known) {
-        if (want == 0 && nfin > c_tot) {
-          next = 1;
-        } else {
-          zk = m_tot;
-          z_known = true;
-        }
+        zk = __fadd_rn(tm0, rest_m);
+        z_known = true;
       }
       if (next < 0 && !p_done) {
         const float target = top_p * zk;
@@ -957,8 +1014,10 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
   for (int j = 0; j < kTrVec; ++j) {
     tr_fence(r[j]);
     float s = 0.f;
+    if (E::vmax(r[j]) >= cut_key) {   // no exponentials for a vector with nothing kept
 #pragma unroll
-    for (int e = 0; e < N; ++e) s += kept_w(E::key(r[j], e));
+      for (int e = 0; e < N; ++e) s += kept_w(E::key(r[j], e));
+    }
     asm volatile("" ::"v"(s));
     ps[j * kTrThreads + tid] = s;
   }
