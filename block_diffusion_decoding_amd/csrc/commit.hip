@@ -840,10 +840,11 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
     };
     // mass of bin i of this thread's 32 (count times the weight of its value), kept
     // out of fused multiply-adds so that the scan and the walk below round alike
+    auto mass_at = [&](uint32_t off, uint32_t cnt) __attribute__((always_inline)) {   // off: below the maximum
+      return cnt == 0 ? 0.f : __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
+    };
     auto bin_mass = [&](uint32_t wbase, int i, uint32_t cnt) __attribute__((always_inline)) {
-      if (cnt == 0) return 0.f;
-      const uint32_t off = wbase + (uint32_t)(tid * kHistPerThread + i);   // bin offset below the maximum
-      return __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
+      return mass_at(wbase + (uint32_t)(tid * kHistPerThread + i), cnt);
     };
     uint32_t c_ex = 0, own_c = 0, c_tot = 0;
     float m_ex = 0.f, own_m = 0.f, m_tot = 0.f;
@@ -863,19 +864,31 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
       m_tot = __fadd_rn(mbase, m_tot);
     };
     // The first bin whose running count reaches k (exact: one thread brackets it).
+    // Its wave walks the bracketing thread's 64 bins, a bin per lane.
     auto find_count = [&](uint32_t wbase, uint32_t k) __attribute__((always_inline)) {
-      if (c_ex < k && k <= c_ex + own_c) {
-        uint32_t cc = c_ex;
-        float lm = 0.f;
-        for (int i = 0; i < kHistPerThread; ++i) {
-          const uint32_t cnt = hist[tid * (kHistPerThread + 1) + i];
-          cc += cnt;
-          lm = __fadd_rn(lm, bin_mass(wbase, i, cnt));
-          if (cc >= k) {
-            sh.cut_off = wbase + (uint32_t)(tid * kHistPerThread + i);
-            sh.cut_mass = __fadd_rn(m_ex, lm);
-            break;
+      if (c_ex < k && k <= c_ex + own_c) sh.first_thr = tid;
+      __syncthreads();
+      const int bt = tr_uni(sh.first_thr);
+      if (wave == bt / 64) {
+        const uint32_t off = wbase + (uint32_t)(bt * kHistPerThread + lane);
+        const uint32_t cnt = hist[bt * (kHistPerThread + 1) + lane];
+        uint32_t cc = cnt;
+        float cm = mass_at(off, cnt);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t yc = __shfl_up(cc, d, 64);
+          const float ym = __shfl_up(cm, d, 64);
+          if (lane >= d) {
+            cc += yc;
+            cm += ym;
           }
+        }
+        const uint32_t cb = __shfl(c_ex, bt & 63, 64);
+        const float mb0 = __shfl(m_ex, bt & 63, 64);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(cb + cc >= k);
+        if (lane == __builtin_ctzll(hit)) {
+          sh.cut_off = off;
+          sh.cut_mass = __fadd_rn(mb0, cm);
         }
       }
       __syncthreads();
