@@ -172,6 +172,11 @@ def main():
             bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
             bd.bd_confidence_commit(logit_pool[i % n_pool], tokens, masked, lw.block_size, T_step, conf=conf,
                                     pred=pred, n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+        for i in range(3):   # sampled commit, plain and with top-p truncation, on all-masked rows
+            for k_, p_ in ((0, 1.0), (0, 0.9)):
+                masked.fill_(1)
+                bd.bd_confidence_commit_sampled(logit_pool[i % n_pool], tokens, masked, lw.block_size, T_step,
+                                                seed=lw.seed, step=i, top_k=k_, top_p=p_)
         torch.cuda.synchronize()
         print("traffic probe done", flush=True)
         return
@@ -573,12 +578,13 @@ def summarize(args):
                     "group by kernel_name, counter_name"):
                 pmc.setdefault(_short(kname), {})[cname] = (n, avg)
         else:
-            out.append(f"## kernel trace: {os.path.basename(dbp)}")
-            out.append(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s}")
-            for kname, n, avg, mn, mx, tot in cur.execute(
-                    "select name, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
-                    "from kernels group by name order by sum(end-start) desc limit 25"):
-                out.append(f"{_short(kname):60s} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} "
+            out.append(f"## kernel trace: {os.path.basename(dbp)} (one line per kernel and grid size)")
+            out.append(f"{'kernel':60s} {'grid':>10s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+                       f"{'total_ms':>10s}")
+            for kname, grid, n, avg, mn, mx, tot in cur.execute(
+                    "select name, grid_x, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
+                    "from kernels group by name, grid_x order by sum(end-start) desc limit 30"):
+                out.append(f"{_short(kname):60s} {grid:10d} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} "
                            f"{tot / 1e6:10.3f}")
             out.append("")
     if pmc:
