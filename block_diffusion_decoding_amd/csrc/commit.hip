@@ -27,6 +27,9 @@
 #ifndef BD_COMMIT_TARGET_WGS
 #define BD_COMMIT_TARGET_WGS 8192
 #endif
+#ifndef BD_SAMPLE_CHUNK_MULT
+#define BD_SAMPLE_CHUNK_MULT 4
+#endif
 
 namespace bd {
 
@@ -36,7 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kStep = 2048;          // vocabulary entries per workgroup and load step (bf16)
 constexpr int kTargetWGs = BD_COMMIT_TARGET_WGS;   // workgroups the chunking aims for
 // Sampling rescans one chunk per row: finer chunks keep that rescan short.
-constexpr int kSampleTargetWGs = 4 * BD_COMMIT_TARGET_WGS;
+constexpr int kSampleTargetWGs = BD_SAMPLE_CHUNK_MULT * BD_COMMIT_TARGET_WGS;
 constexpr int kMinChunk = 4096;      // fewest vocabulary entries per chunk
 constexpr int kDecideLanes = 8;      // threads merging one row's partials
 constexpr int kMergeBatch = 8;       // partial loads in flight per merging thread

@@ -104,7 +104,8 @@ def run_case(logits_np, dtype, tokens, masked, blk_len, T, tau, seed, step, top_
     return gpu
 
 
-KP = [(1, 1.0), (5, 1.0), (50, 1.0), (0, 0.1), (0, 0.5), (0, 0.9), (50, 0.9), (1000, 0.95)]
+# (top_k, top_p); the last keeps every id (top-k beyond the vocabulary) through the truncating kernel
+KP = [(1, 1.0), (5, 1.0), (50, 1.0), (0, 0.1), (0, 0.5), (0, 0.9), (50, 0.9), (1000, 0.95), (10**6, 1.0)]
 
 
 @pytest.mark.parametrize("k,p", KP)
