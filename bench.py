@@ -284,6 +284,39 @@ def main():
 
     loops = [full_loop(T) for T in lw.thresholds]
 
+    def graph_loop(T, reps=3):
+        """The same loop with each step (decode, commit, read-back of the block counts) replayed
+        from a captured graph: one graph per logits buffer of the pool."""
+        graphs = []
+        for i in range(n_pool):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
+                bd.bd_confidence_commit(logit_pool[i], tokens, masked, lw.block_size, T, conf=conf, pred=pred,
+                                        n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+                nleft_host.copy_(nleft, non_blocking=True)
+            graphs.append(g)
+        steps_all, t_all = [], 0.0
+        for _ in range(reps):
+            masked.fill_(1)
+            tokens.fill_(-1)
+            torch.cuda.synchronize()
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                graphs[n % n_pool].replay()
+                torch.cuda.current_stream().synchronize()
+                n += 1
+                if int(nleft_host.sum()) == 0 or n >= 4 * lw.block_size:
+                    break
+            t_all += time.perf_counter() - t0
+            steps_all.append(n)
+        del graphs
+        return {"T": T, "steps_per_block": steps_all[0], "steps_per_s": round(sum(steps_all) / t_all, 1),
+                "tokens_per_s": round(n_rows * reps / t_all, 1)}
+
+    loops_graph = [graph_loop(T) for T in lw.thresholds]
+
     # the same decode step with the prefix in shuffled pages of 256 rows (bd_attn_decode_block_paged)
     page = 256
     max_pages = (max_p + page - 1) // page
@@ -501,7 +534,7 @@ def main():
                             round(rw_bytes / (np.median(tr_us[(50, 1.0)]) * 1e-6) / 1e9, 1),
                         "commit_sampled_topp0.9_GBps_first_step":
                             round(rw_bytes / (np.median(tr_us[(0, 0.9)]) * 1e-6) / 1e9, 1),
-                        "by_threshold": loops},
+                        "by_threshold": loops, "by_threshold_graph_replay": loops_graph},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(dec1_us, 90)), 2),
