@@ -843,8 +843,9 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
     };
     // mass of bin i of this thread's 32 (count times the weight of its value), kept
     // out of fused multiply-adds so that the scan and the walk below round alike
+    // (masses are only needed for top-p: with top-k alone the counts place the cut)
     auto mass_at = [&](uint32_t off, uint32_t cnt) __attribute__((always_inline)) {   // off: below the maximum
-      return cnt == 0 ? 0.f : __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
+      return (cnt == 0 || !need_p) ? 0.f : __fmul_rn((float)cnt, weight(E::value_of_key(kmax - off)));
     };
     auto bin_mass = [&](uint32_t wbase, int i, uint32_t cnt) __attribute__((always_inline)) {
       return mass_at(wbase + (uint32_t)(tid * kHistPerThread + i), cnt);
