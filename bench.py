@@ -35,6 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# Mean steps per block of the 64-sequence loop under its logits recipe (N(0,1) plus a U(2, 14)
+# boost at one id per row, vocabulary 151936, fresh every step), by Monte Carlo of the recipe.
+EXPECTED_STEPS = {0.5: 15.9, 0.95: 31.9, 0.99: 32.0}
 
 
 def parse():
@@ -114,7 +117,10 @@ def main():
     V = lw.vocab
     gen = torch.Generator(device=dev)
     gen.manual_seed(lw.seed)
-    n_pool = 4
+    # Fresh logits for every step of a loop: with the fallback a block finishes within block_size
+    # steps, so one buffer per step (32 x 622 MB, resident in HBM) gives every step of every loop
+    # its own draw; the generator runs before any timed region.
+    n_pool = lw.block_size
     logit_pool = []
     for _ in range(n_pool):   # N(0,1) + U(2,14) at one random id per row, bf16
         x = torch.randn((n_rows, V), generator=gen, device=dev, dtype=torch.float32)
@@ -258,15 +264,29 @@ def main():
     com_gbs_loop = [r * V * 2 / (u * 1e-6) / 1e9 for r, u in zip(com_rows, com_us)]
 
     # ------------------------------------------- decode-loop steps/s per T
+    def loop_record(T, steps_all, blk_steps, t_all, reps):
+        """steps/s of the whole loops, and the steps each sequence's block took (mean over the
+        sequences and runs, and the largest), beside the values the workload's recipe predicts."""
+        bs = np.concatenate(blk_steps)
+        return {"T": T, "loop_steps": steps_all[0], "steps_per_block_mean": round(float(bs.mean()), 2),
+                "steps_per_block_max": int(bs.max()), "steps_per_block_expected_mean": EXPECTED_STEPS.get(T),
+                "steps_per_s": round(sum(steps_all) / t_all, 1), "tokens_per_s": round(n_rows * reps / t_all, 1)}
+
+    def block_steps(left_per_step):
+        """Per sequence, the step count at which its block had no masked row left."""
+        left = np.stack(left_per_step)                   # [steps, n_seq]
+        return (left > 0).sum(axis=0) + 1
+
     def full_loop(T, reps=3):
-        """Whole loops from an all-masked block until every sequence's block is committed;
-        wall-clock steps/s including the per-step read-back of the block counts."""
-        steps_all, t_all = [], 0.0
+        """Whole loops from an all-masked block until every sequence's block is committed, with
+        fresh logits at every step; wall-clock steps/s including the per-step read-back of the
+        block counts."""
+        steps_all, blk_steps, t_all = [], [], 0.0
         for _ in range(reps):
             masked.fill_(1)
             tokens.fill_(-1)
             torch.cuda.synchronize()
-            n = 0
+            n, left = 0, []
             t0 = time.perf_counter()
             while True:
                 bd.bd_attn_decode_block(qb, kb, vb, kc, vc, ps, pl, max_p, o=dec_o, lse=dec_lse, workspace=dec_ws)
@@ -275,18 +295,19 @@ def main():
                 nleft_host.copy_(nleft, non_blocking=True)
                 torch.cuda.current_stream().synchronize()
                 n += 1
-                if int(nleft_host.sum()) == 0 or n >= 4 * lw.block_size:
+                left.append(nleft_host.numpy().copy())
+                if int(nleft_host.sum()) == 0 or n >= n_pool:
                     break
             t_all += time.perf_counter() - t0
             steps_all.append(n)
-        return {"T": T, "steps_per_block": steps_all[0], "steps_per_s": round(sum(steps_all) / t_all, 1),
-                "tokens_per_s": round(n_rows * reps / t_all, 1)}
+            blk_steps.append(block_steps(left))
+        return loop_record(T, steps_all, blk_steps, t_all, reps)
 
     loops = [full_loop(T) for T in lw.thresholds]
 
     def graph_loop(T, reps=3):
         """The same loop with each step (decode, commit, read-back of the block counts) replayed
-        from a captured graph: one graph per logits buffer of the pool."""
+        from a captured graph: one graph per step's logits buffer."""
         graphs = []
         for i in range(n_pool):
             g = torch.cuda.CUDAGraph()
@@ -296,24 +317,25 @@ def main():
                                         n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
                 nleft_host.copy_(nleft, non_blocking=True)
             graphs.append(g)
-        steps_all, t_all = [], 0.0
+        steps_all, blk_steps, t_all = [], [], 0.0
         for _ in range(reps):
             masked.fill_(1)
             tokens.fill_(-1)
             torch.cuda.synchronize()
-            n = 0
+            n, left = 0, []
             t0 = time.perf_counter()
             while True:
                 graphs[n % n_pool].replay()
                 torch.cuda.current_stream().synchronize()
                 n += 1
-                if int(nleft_host.sum()) == 0 or n >= 4 * lw.block_size:
+                left.append(nleft_host.numpy().copy())
+                if int(nleft_host.sum()) == 0 or n >= n_pool:
                     break
             t_all += time.perf_counter() - t0
             steps_all.append(n)
+            blk_steps.append(block_steps(left))
         del graphs
-        return {"T": T, "steps_per_block": steps_all[0], "steps_per_s": round(sum(steps_all) / t_all, 1),
-                "tokens_per_s": round(n_rows * reps / t_all, 1)}
+        return loop_record(T, steps_all, blk_steps, t_all, reps)
 
     loops_graph = [graph_loop(T) for T in lw.thresholds]
 
@@ -492,7 +514,30 @@ def main():
     # --------------------------------------------------------- CPU oracle sample
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        # the first loop step's inputs and the GPU's commit of it, for 4 of the 64 sequences
+        sample_seqs = [0, 16, 32, 48]
+        masked.fill_(1)
+        tokens.fill_(-1)
+        bd.bd_confidence_commit(logit_pool[0], tokens, masked, lw.block_size, 0.95, conf=conf, pred=pred,
+                                n_committed=ncom, n_masked_left=nleft, workspace=com_ws)
+        torch.cuda.synchronize()
+        rows = np.concatenate([np.arange(s_ * lw.block_size, (s_ + 1) * lw.block_size) for s_ in sample_seqs])
+        rows_t = torch.from_numpy(rows).to(dev)
+        ps_np, pl_np = ps.cpu().numpy(), pl.cpu().numpy()
+
+        def host_bits(t):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        loop_sample = {
+            "seqs": sample_seqs,
+            "q_blk": host_bits(qb[sample_seqs]), "k_blk": host_bits(kb[sample_seqs]), "v_blk": host_bits(vb[sample_seqs]),
+            "k_cache": [host_bits(kc[int(ps_np[s_]):int(ps_np[s_]) + int(pl_np[s_])]) for s_ in sample_seqs],
+            "v_cache": [host_bits(vc[int(ps_np[s_]):int(ps_np[s_]) + int(pl_np[s_])]) for s_ in sample_seqs],
+            "logits": host_bits(logit_pool[0][rows_t]),
+            "gpu_conf": conf[rows_t].cpu().numpy(), "gpu_pred": pred[rows_t].cpu().numpy(),
+            "n_seq": lw.n_seq, "thresholds": lw.thresholds,
+        }
+        cfg2 = {"decode": d1, "logits": c1["logits"], "threshold": sw.threshold}
+        cpu = cpu_baseline(wl, args.cpu_seconds, cfg2, loop_sample)
 
     ms_per_step = wall / args.steps * 1e3
     line = {
@@ -561,6 +606,7 @@ def main():
 KERNEL_SRC = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
 REF_COPY_KERNEL = "bitwise_not_kernel"     # the counter-scale reference kernel of the traffic probe
 REF_COPY_BYTES = 1 << 30
+SIMD_NUM = 256 * 4                          # MI355X: 256 compute units of 4 SIMDs
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -600,7 +646,7 @@ def summarize(args):
     """Write a short text summary of rocprofv3 result databases (kernel trace or counters)."""
     import sqlite3
     out = [f"# {args.title}".rstrip(), f"# command: {args.command}", f"# kernel sources: src={kernel_source_hash()}", ""]
-    pmc = {}
+    pmc, trace_us = {}, {}
     for dbp in args.summarize:
         db = sqlite3.connect(dbp)
         cur = db.cursor()
@@ -611,6 +657,8 @@ def summarize(args):
                     "group by kernel_name, counter_name"):
                 pmc.setdefault(_short(kname), {})[cname] = (n, avg)
         else:
+            for kname, n, avg in cur.execute("select name, count(*), avg(end-start) from kernels group by name"):
+                trace_us[_short(kname)] = avg / 1e3
             out.append(f"## kernel trace: {os.path.basename(dbp)} (one line per kernel and grid size)")
             out.append(f"{'kernel':60s} {'grid':>10s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
                        f"{'total_ms':>10s}")
@@ -628,6 +676,32 @@ def summarize(args):
             if not kname:
                 continue
             out.append(f"{kname:60s} " + " ".join(f"{d[c][1]:26.6g}" if c in d else f"{'-':>26s}" for c in names))
+        mf = [(k, d) for k, d in sorted(pmc.items()) if k and ("SQ_VALU_MFMA_BUSY_CYCLES" in d
+                                                                or "SQ_INSTS_VALU_MFMA_MOPS_BF16" in d)]
+        if mf:
+            out.append("")
+            out.append(f"## matrix-core use per dispatch (SIMDs = {SIMD_NUM}); busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                       "(GRBM_GUI_ACTIVE x SIMDs) (the MfmaUtil expression of rocprofv3's counter definitions); "
+                       "bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; avg_us from the kernel trace of the "
+                       "same program")
+            out.append(f"{'kernel':40s} {'mfma_busy':>10s} {'gui_cycles':>12s} {'avg_us':>10s} {'gui_MHz':>9s} "
+                       f"{'bf16_TFLOP':>11s} {'TFLOP/s':>9s} {'lds_confl/inst':>15s}")
+            for kname, d in mf:
+                busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", (0, None))[1]
+                gui = d.get("GRBM_GUI_ACTIVE", (0, None))[1]
+                mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0, None))[1]
+                lds = d.get("SQ_INSTS_LDS", (0, None))[1]
+                confl = d.get("SQ_LDS_BANK_CONFLICT", (0, None))[1]
+                us = trace_us.get(kname)
+                util = busy / (gui * SIMD_NUM) if busy is not None and gui else None
+                tfl = mops * 512 / 1e12 if mops is not None else None
+
+                def fmt(x, w, f):
+                    return f"{x:{w}{f}}" if x is not None else f"{'-':>{w}s}"
+                out.append(f"{kname[:40]:40s} {fmt(util, 10, '.4f')} {fmt(gui, 12, '.0f')} {fmt(us, 10, '.2f')} "
+                           f"{fmt(gui / us if gui and us else None, 9, '.0f')} {fmt(tfl, 11, '.4f')} "
+                           f"{fmt(tfl / (us * 1e-6) if tfl is not None and us else None, 9, '.1f')} "
+                           f"{fmt(confl / lds if confl is not None and lds else None, 15, '.4f')}")
         copy = next((d for k, d in pmc.items() if REF_COPY_KERNEL in k), None)
         if copy and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
             ref_kib = REF_COPY_BYTES / 1024.0
@@ -647,11 +721,21 @@ def summarize(args):
     print(text)
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The oracle forward on a bounded sample of the same workload: whole (batch, head)
-    pairs of the 16384-token workload, one after another until the time budget is spent."""
+def cpu_baseline(wl, budget_s: float, cfg2: dict, loop_sample: dict):
+    """The oracle, as it stands, on bounded samples of the same workloads.
+
+    Headline: the oracle forward on whole (batch, head) pairs of the 16384-token workload, one
+    after another until the time budget is spent (TFLOP/s on the allowed pairs).  Beside it:
+    the 4096-prefix decode step and its 32-row commit in full (GB/s of the same algorithmic
+    bytes as the GPU figures), the backward on the last 1024 tokens of one (batch, KV head)
+    group of the 16384-token workload (TFLOP/s, 2.5x count), and one step of the 64-sequence loop
+    on 4 of its sequences (block attention + commit; steps/s scaled to 64 sequences).  The
+    oracle commit of those 128 first-step rows also gives the near-T accounting of the loop's
+    first step (rows whose confidence lies within 1e-4 of each T) and a spot check of the GPU's
+    ids and confidences on them."""
     import workloads as W
     from oracle import attention as OA
+    from oracle import commit as OC
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
@@ -660,9 +744,13 @@ def cpu_baseline(wl, budget_s: float):
     rng = np.random.default_rng(wl.seed)
     L, D, blk = wl.seqlen, wl.head_dim, wl.block_size
 
-    def draw():
-        x = rng.standard_normal((1, L, 1, D), dtype=np.float32)
+    def draw(heads=1):
+        x = rng.standard_normal((1, L, heads, D), dtype=np.float32)
         return W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
+
+    def f64(bits):
+        return W.bf16_bits_to_f32(bits).astype(np.float64)
+
     flops_pair = OA.attn_flops(L, blk, 1, D)
     done, pairs = 0.0, 0
     t_work = 0.0
@@ -673,9 +761,64 @@ def cpu_baseline(wl, budget_s: float):
         t_work += time.perf_counter() - t0
         done += flops_pair
         pairs += 1
+    legs = {}
+
+    # the 4096-prefix decode step and the commit of its [32 x 151936] logits, in full
+    d = cfg2["decode"]
+    Hkv, Dd = d["k_blk"].shape[2], d["k_blk"].shape[3]
+    P = int(d["prefix_len"][0])
+    args_ = [f64(d[n]) for n in ("q_blk", "k_blk", "v_blk", "k_cache", "v_cache")]
+    t0 = time.perf_counter()
+    OA.decode_block(*args_, d["prefix_start"], d["prefix_len"])
+    t_dec = time.perf_counter() - t0
+    dec_bytes = (P + d["k_blk"].shape[1]) * Hkv * Dd * 2 * 2
+    lg = W.bf16_bits_to_f32(cfg2["logits"])
+    R = lg.shape[0]
+    t0 = time.perf_counter()
+    OC.confidence_commit(lg, np.full(R, -1, np.int32), np.ones(R, np.uint8), R, cfg2["threshold"])
+    t_com = time.perf_counter() - t0
+    legs["decode_step_4096"] = {"GBps": round(dec_bytes / t_dec / 1e9, 4), "s": round(t_dec, 3)}
+    legs["commit_32x151936"] = {"GBps": round(lg.size * 2 / t_com / 1e9, 4), "s": round(t_com, 3)}
+
+    # backward on the last 1024 tokens of one group (2 query heads sharing one KV head)
+    G = wl.n_q_heads // wl.n_kv_heads
+    q, do = draw(G), draw(G)
+    k, v = draw(), draw()
+    qb0 = (L - 1024) // blk
+    t0 = time.perf_counter()
+    OA.attn_bwd(q, k, v, do, blk, q_block_start=qb0)
+    t_bwd = time.perf_counter() - t0
+    slice_pairs = sum(blk * min(L, (b + 1) * blk) for b in range(qb0, L // blk))
+    bwd_flops = 2.5 * 4.0 * D * slice_pairs * G
+    legs["bwd_last1024_one_group"] = {"TFLOPs_2.5x": round(bwd_flops / t_bwd / 1e12, 5), "s": round(t_bwd, 3)}
+
+    # one loop step on 4 of the 64 sequences: block attention against each prefix, then the commit
+    ls = loop_sample
+    n4 = len(ls["seqs"])
+    plen = np.array([c.shape[0] for c in ls["k_cache"]], np.int64)
+    pstart = np.concatenate([[0], np.cumsum(plen)[:-1]])
+    kcache = np.concatenate([f64(c) for c in ls["k_cache"]])
+    vcache = np.concatenate([f64(c) for c in ls["v_cache"]])
+    qs, ks, vs = f64(ls["q_blk"]), f64(ls["k_blk"]), f64(ls["v_blk"])
+    lg = W.bf16_bits_to_f32(ls["logits"])
+    Rs = lg.shape[0]
+    t0 = time.perf_counter()
+    OA.decode_block(qs, ks, vs, kcache, vcache, pstart, plen)
+    ref = OC.confidence_commit(lg, np.full(Rs, -1, np.int32), np.ones(Rs, np.uint8), Rs // n4, 0.95)
+    t_step = time.perf_counter() - t0
+    legs["loop_step_4_of_64_seqs"] = {"steps_per_s_scaled_to_64": round(n4 / (ls["n_seq"] * t_step), 4),
+                                      "s": round(t_step, 3)}
+    # near-T accounting and spot check of the GPU's first-step commit on these rows
+    c = ref["conf"]
+    near = {str(T): int((np.abs(c - T) <= 1e-4).sum()) for T in ls["thresholds"]}
+    valid = ~np.isnan(c)
+    rel = float(np.max(np.abs(ls["gpu_conf"][valid] - c[valid]) / c[valid])) if valid.any() else 0.0
+    check = {"rows": int(Rs), "band": 1e-4, "near_T_rows": near,
+             "pred_equal": bool(np.array_equal(ls["gpu_pred"], ref["pred"])), "conf_max_rel_err": rel}
     return {"value": round(done / t_work / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"numpy fp64 oracle forward over {pairs} of the {wl.batch * wl.n_q_heads} (batch, head) "
-                      f"pairs of the {L}-token workload ({done / 1e9:.0f} GFLOP in {t_work:.1f} s)"}
+                      f"pairs of the {L}-token workload ({done / 1e9:.0f} GFLOP in {t_work:.1f} s)",
+            "legs": legs, "first_loop_step_check": check}
 
 
 if __name__ == "__main__":

@@ -5,8 +5,10 @@ uses); the oracle recomputes O from the definition.  Tolerance on dQ, dK, dV:
 max-abs <= tol * max(1, max|ref|) with tol = 2e-2 for bf16 (as for the forward
 output) and 2e-5 for fp32 (fp32 sums of up to L products, each within a few
 ulp).  The 2 x 16384-token workload runs in full on the GPU and is compared on
-its last 1024 tokens: dK/dV of those keys depend only on queries in the slice,
-and dQ of those queries sees every key.
+its last 1024 tokens (dK/dV of those keys depend only on queries in the slice,
+and dQ of those queries sees every key) and, for one (batch, KV head) group, on
+every key and query: the first keys' dK/dV sum over all 16384 queries of both
+query heads of the group, the longest accumulation chains of the kernel.
 """
 import numpy as np
 import pytest
@@ -89,3 +91,15 @@ def test_full_size_workload_last_1024_tokens():
     for g in grads:
         assert torch.isfinite(g.float()).all()
     check(inp, "bf16", wl.block_size, grads, q_block_start=(wl.seqlen - 1024) // wl.block_size)
+    # one whole group: batch 1, KV head 5 and its query heads 10, 11, all keys and queries
+    b, g = 1, 5
+    G = wl.n_q_heads // wl.n_kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    f = {n: host_vals(inp[n][b:b + 1, :, hs if n in ("q", "do") else slice(g, g + 1)], "bf16")
+         for n in ("q", "k", "v", "do")}
+    rq, rk, rv = OA.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.block_size)
+    compare("dk group (all keys)", to_np(grads[1])[b:b + 1, :, g:g + 1], rk, "bf16")
+    compare("dv group (all keys)", to_np(grads[2])[b:b + 1, :, g:g + 1], rv, "bf16")
+    compare("dk keys [0, 1024)", to_np(grads[1])[b:b + 1, :1024, g:g + 1], rk[:, :1024], "bf16")
+    compare("dv keys [0, 1024)", to_np(grads[2])[b:b + 1, :1024, g:g + 1], rv[:, :1024], "bf16")
+    compare("dq group (all queries)", to_np(grads[0])[b:b + 1, :, hs], rq, "bf16")

@@ -162,6 +162,37 @@ def test_loop_scripted_schedule():
     assert list(res["tokens"]) == [r % V for r in range(blk)]
 
 
+def test_loop_with_sampled_commit():
+    """The loop with the sampled commit rule in place of the greedy one.  (i) The scripted
+    schedule above at temperature 0.05: a confident row's boosted id then holds all but
+    e^-136 of the probability, so every draw takes it and the schedule, the commit steps and the
+    tokens are those of the greedy loop.  (ii) T >= 1 stays token-level: one fallback commit per
+    step whatever the rule, so a block of L' tokens takes exactly L' steps."""
+    from oracle import sampling as S
+    blk, V = 8, 10
+
+    def logits(step):
+        x = np.zeros((blk, V))
+        for r in range(blk):
+            if r // 2 <= step:
+                x[r, r % V] = math.log(0.99 * (V - 1) / 0.01)
+        return x
+
+    def sampled(tau, seed):
+        return lambda lg, tok, msk, b, T, fb, step: S.sampled_commit(lg, tok, msk, b, T, tau, seed, step, fb)
+
+    res = DL.decode_loop(1, blk, logits, 0.95, commit=sampled(0.05, 11))
+    assert res["steps"][0] == 4
+    assert list(res["commit_step"]) == [0, 0, 1, 1, 2, 2, 3, 3]
+    assert list(res["tokens"]) == [r % V for r in range(blk)]
+    rng = np.random.default_rng(5)
+    n = 3
+    res = DL.decode_loop(n, blk, lambda s: rng.standard_normal((n * blk, V)), 1.0, commit=sampled(1.0, 12))
+    assert list(res["steps"]) == [blk] * n and not res["masked"].any()
+    for g in range(n):
+        assert sorted(res["commit_step"][g * blk:(g + 1) * blk]) == list(range(blk))
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_loop_bounds(seed):
     rng = np.random.default_rng(seed)

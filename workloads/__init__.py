@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "Workload", "WORKLOADS",
     "attention_inputs", "decode_inputs", "commit_inputs", "prefix_lengths",
-    "boosted_logits_bits",
+    "boosted_logits_bits", "loop_step_logits", "loop_step_block", "lmhead_inputs",
 ]
 
 
@@ -45,13 +45,16 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     stays +-Inf.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    u = x.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # at most 0xFF807FFF for finite and infinite inputs: no 32-bit overflow
+    r >>= 16
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r = np.where(nan, (u >> 16).astype(np.uint32) | 0x40, r)
-    return r.astype(np.uint16)
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -195,6 +198,25 @@ def boosted_logits_bits(rows: int, vocab: int, boost_lo: float, boost_hi: float,
     ids = rng.integers(0, vocab, size=rows)
     x[np.arange(rows), ids] += rng.uniform(boost_lo, boost_hi, size=rows).astype(np.float32)
     return _as_dtype(x, dtype)
+
+
+def loop_step_logits(n_seq: int, blk_len: int, vocab: int, boost: tuple, seed: int, step: int,
+                     dtype: str = "bf16") -> np.ndarray:
+    """Fresh logits of one step of the decode loop: ``[n_seq*blk_len, vocab]`` drawn as
+    ``boosted_logits_bits`` from a generator seeded by ``(seed, step)``, so any step can be
+    drawn again on its own."""
+    rng = np.random.default_rng((seed, step))
+    return boosted_logits_bits(n_seq * blk_len, vocab, boost[0], boost[1], rng, dtype)
+
+
+def loop_step_block(n_seq: int, blk_len: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                    dtype: str, seed: int, step: int) -> dict:
+    """Fresh q_blk / k_blk / v_blk of one step of the decode loop (N(0,1)), from a generator
+    seeded by ``(seed, step, 1)``."""
+    rng = np.random.default_rng((seed, step, 1))
+    return {"q_blk": _as_dtype(_normal(rng, (n_seq, blk_len, n_q_heads, head_dim)), dtype),
+            "k_blk": _as_dtype(_normal(rng, (n_seq, blk_len, n_kv_heads, head_dim)), dtype),
+            "v_blk": _as_dtype(_normal(rng, (n_seq, blk_len, n_kv_heads, head_dim)), dtype)}
 
 
 def commit_inputs(n_seq: int, blk_len: int, vocab: int, dtype: str, seed: int,
