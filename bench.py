@@ -607,6 +607,7 @@ KERNEL_SRC = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
 REF_COPY_KERNEL = "bitwise_not_kernel"     # the counter-scale reference kernel of the traffic probe
 REF_COPY_BYTES = 1 << 30
 SIMD_NUM = 256 * 4                          # MI355X: 256 compute units of 4 SIMDs
+N_XCD = 8                                   # ... in 8 XCDs
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -680,15 +681,17 @@ def summarize(args):
                                                                 or "SQ_INSTS_VALU_MFMA_MOPS_BF16" in d)]
         if mf:
             out.append("")
-            out.append(f"## matrix-core use per dispatch (SIMDs = {SIMD_NUM}); busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-                       "(GRBM_GUI_ACTIVE x SIMDs) (the MfmaUtil expression of rocprofv3's counter definitions); "
-                       "bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; avg_us from the kernel trace of the "
-                       "same program")
-            out.append(f"{'kernel':40s} {'mfma_busy':>10s} {'gui_cycles':>12s} {'avg_us':>10s} {'gui_MHz':>9s} "
+            out.append(f"## matrix-core use per dispatch; busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the "
+                       f"{SIMD_NUM} SIMDs) / (SIMDs x active cycles), active cycles = GRBM_GUI_ACTIVE / {N_XCD} "
+                       "(the counter comes back summed over the XCDs; rocprofv3's MfmaUtil takes their maximum); "
+                       "bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; avg_us from the kernel trace of the same "
+                       "program (another run), clk = active cycles / avg_us")
+            out.append(f"{'kernel':40s} {'mfma_busy':>10s} {'cycles/XCD':>12s} {'avg_us':>10s} {'clk_MHz':>9s} "
                        f"{'bf16_TFLOP':>11s} {'TFLOP/s':>9s} {'lds_confl/inst':>15s}")
             for kname, d in mf:
                 busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", (0, None))[1]
                 gui = d.get("GRBM_GUI_ACTIVE", (0, None))[1]
+                gui = gui / N_XCD if gui is not None else None
                 mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0, None))[1]
                 lds = d.get("SQ_INSTS_LDS", (0, None))[1]
                 confl = d.get("SQ_LDS_BANK_CONFLICT", (0, None))[1]

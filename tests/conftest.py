@@ -20,7 +20,7 @@ def golden_dir():
 def pytest_terminal_summary(terminalreporter):
     """Near-T accounting of the commit parity tests: rows whose oracle confidence lies within 1e-4
     of T are not graded bit-exactly, and groups decided by such rows (or by a fallback between
-    confidences within 1e-4 of each other) are checked for validity only; their counts are
+    confidences within a relative 1e-4 of each other) are checked for validity only; their counts are
     reported here so that they survive a quiet run."""
     gu = sys.modules.get("gpu_util")
     log = getattr(gu, "NEAR_T_LOG", None) if gu is not None else None

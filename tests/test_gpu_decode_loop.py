@@ -14,7 +14,7 @@ replays the loop over the very same bytes.
 Grading:
   * each step is graded against the oracle's commit applied to the GPU's own state before the
     step (ids and masks bit-exact; groups with a row within 1e-4 of T, or a fallback decided by
-    confidences within 1e-4 of each other, are checked for validity only and flagged);
+    confidences within a relative 1e-4 of each other, are checked for validity only and flagged);
   * a finished block is a no-op: its rows are unchanged and it reports 0 committed, 0 left;
   * the whole loop is replayed by oracle.decode_loop from the all-masked start: for every
     sequence never flagged, the steps its block took, the step at which each row was committed
