@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (BD_BF16, BD_F32, BD_FALLBACK_NONE, BD_FALLBACK_TOP1, BdError, check, lib)
 
 __all__ = [
-    "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit",
+    "bd_attn_fwd", "bd_attn_bwd", "bd_attn_decode_block", "bd_confidence_commit", "bd_confidence_commit_noalloc",
     "bd_confidence_commit_rowwise", "bd_lmhead_commit", "bd_lmhead_commit_workspace_size",
     "bd_confidence_commit_sampled", "bd_confidence_commit_sampled_workspace_size",
     "bd_attn_decode_block_paged", "bd_kv_append_block",
@@ -181,6 +181,28 @@ def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold, fallba
                                       _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb,
                                       _stream(stream))
         check(st, "bd_confidence_commit")
+    return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}
+
+
+def bd_confidence_commit_noalloc(logits, tokens, masked, blk_len: int, threshold: float,
+                                 fallback: int = BD_FALLBACK_TOP1, vocab: Optional[int] = None, conf=None, pred=None,
+                                 n_committed=None, n_masked_left=None, stream=None):
+    """bd_confidence_commit with the library's fixed device scratch in place of a workspace (the
+    C entry point allocates nothing; outputs not passed in are allocated here).  Updates
+    ``tokens``/``masked`` in place; returns dict(conf, pred, n_committed, n_masked_left)."""
+    rows = logits.shape[0]
+    if rows % blk_len:
+        raise ValueError("logits rows must be a multiple of blk_len")
+    n_seq = rows // blk_len
+    V = logits.shape[1] if vocab is None else int(vocab)
+    if not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
+    _need(tokens, "tokens", (rows,), torch.int32)
+    _need(masked, "masked", (rows,), torch.uint8)
+    st = lib.bd_confidence_commit_noalloc(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
+                                          float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf),
+                                          _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _stream(stream))
+    check(st, "bd_confidence_commit_noalloc")
     return {"conf": conf, "pred": pred, "n_committed": n_committed, "n_masked_left": n_masked_left}
 
 

@@ -12,7 +12,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BD_LIBRARY") or os.path.join(_HERE, "libbd.so")
 
 BD_OK, BD_ERR_NULL, BD_ERR_SHAPE, BD_ERR_UNSUPPORTED, BD_ERR_WORKSPACE, BD_ERR_VALUE, BD_ERR_HIP, \
-    BD_ERR_ALIGNMENT = range(8)
+    BD_ERR_ALIGNMENT, BD_ERR_SCRATCH = range(9)
+BD_NOALLOC_SCRATCH_BYTES = 4 << 20   # include/bd.h
 BD_F32, BD_BF16 = 0, 1
 BD_FALLBACK_NONE, BD_FALLBACK_TOP1 = 0, 1
 
@@ -37,6 +38,7 @@ _SIGS = {
                                   _p]),
     "bd_confidence_commit_workspace_size": (_sz, [_i, _i, _i]),
     "bd_confidence_commit": (_i, [_p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "bd_confidence_commit_noalloc": (_i, [_p, _i64, _i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p]),
     "bd_confidence_commit_rowwise": (_i, [_p, _i64, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "bd_attn_decode_block_paged": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p,
                                         _sz, _p]),

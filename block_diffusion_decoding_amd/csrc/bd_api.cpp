@@ -42,7 +42,7 @@ bd_status check_attn_shape(int batch, int seqlen, int hq, int hkv, int d, int bl
 bd_status commit_common(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab, bd_dtype dtype,
                         float threshold, const float* thresholds, bd_fallback fallback, int32_t* tokens,
                         uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed, int32_t* n_masked_left,
-                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+                        void* workspace, size_t ws_bytes, hipStream_t stream, bool noalloc = false) {
   if (!logits || !tokens || !masked) return BD_ERR_NULL;
   if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || row_stride < vocab) return BD_ERR_SHAPE;
   if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
@@ -52,11 +52,17 @@ bd_status commit_common(const void* logits, int64_t row_stride, int n_seq, int b
   const long long rows = (long long)n_seq * blk_len;
   if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
   const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab);
-  if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > bd::kNoAllocScratchBytes) return BD_ERR_SCRATCH;
+  } else if (!workspace || ws_bytes < need) {
+    return BD_ERR_WORKSPACE;
+  }
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, thresholds,
                    fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
-  return hip_status(bd::launch_commit(a, stream));
+  return hip_status(noalloc ? bd::launch_commit_noalloc(a, stream) : bd::launch_commit(a, stream));
 }
+
+static_assert(bd::kNoAllocScratchBytes == BD_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the kernels");
 
 }  // namespace
 
@@ -72,6 +78,7 @@ const char* bd_status_string(bd_status s) {
     case BD_ERR_VALUE: return "scalar argument out of its domain";
     case BD_ERR_HIP: return "HIP runtime error";
     case BD_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case BD_ERR_SCRATCH: return "problem exceeds the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -219,6 +226,14 @@ bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq
                                int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return commit_common(logits, row_stride, n_seq, blk_len, vocab, dtype, threshold, nullptr, fallback, tokens,
                        masked, conf, pred, n_committed, n_masked_left, workspace, ws_bytes, stream);
+}
+
+bd_status bd_confidence_commit_noalloc(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, float threshold, bd_fallback fallback, int32_t* tokens,
+                                       uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
+                                       int32_t* n_masked_left, hipStream_t stream) {
+  return commit_common(logits, row_stride, n_seq, blk_len, vocab, dtype, threshold, nullptr, fallback, tokens,
+                       masked, conf, pred, n_committed, n_masked_left, nullptr, 0, stream, true);
 }
 
 bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,

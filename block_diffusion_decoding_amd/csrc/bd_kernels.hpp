@@ -71,6 +71,10 @@ struct CommitArgs {
 int commit_chunks_per_row(long long rows, int vocab);
 size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+// The same with the partials in the library's fixed device scratch array (a.ws is ignored);
+// the caller has checked commit_workspace_bytes() <= kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+hipError_t launch_commit_noalloc(const CommitArgs& a, hipStream_t st);
 // Sampled predictions at `temperature` (Philox4x32-10 keyed by seed, row, step).
 size_t commit_sampled_workspace_bytes(int n_seq, int blk_len, int vocab);
 hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,

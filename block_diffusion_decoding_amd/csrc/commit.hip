@@ -1251,6 +1251,46 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   return launch_commit_decide(part, nchunk, a, st);
 }
 
+// ---- no-allocation variant ---------------------------------------------------
+// The chunk partials of bd_confidence_commit_noalloc live in this array, one copy
+// per GPU (loaded with the code object).  In host code `scratch` names a host-side
+// stand-in: kernels get the device address looked up below, never the name.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+}  // namespace
+
+// Device address of `scratch` on the calling thread's current device.
+static hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_commit_noalloc(const CommitArgs& a, hipStream_t st) {
+  if (commit_workspace_bytes(a.n_seq, a.blk_len, a.vocab) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  CommitArgs b = a;
+  b.ws = ws;
+  return launch_commit(b, st);
+}
+
 hipError_t launch_commit_decide(const void* part, int nchunk, const CommitArgs& a, hipStream_t st) {
   return launch_decide(part, nchunk, nullptr, nullptr, a, st);
 }

@@ -32,8 +32,9 @@
  *     gives the hipError_t).  Faults inside a kernel surface at the caller's
  *     next synchronisation.
  *   - The library keeps no mutable global state except a thread-local last HIP
- *     error; calls on different streams may run concurrently as long as their
- *     output and workspace buffers do not overlap.
+ *     error (and, for bd_confidence_commit_noalloc only, a fixed device scratch
+ *     array per GPU); calls on different streams may run concurrently as long as
+ *     their output and workspace buffers do not overlap.
  */
 #ifndef BD_H_
 #define BD_H_
@@ -54,7 +55,9 @@ typedef enum {
   BD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query returns */
   BD_ERR_VALUE = 5,        /* a scalar argument is out of its domain (e.g. NaN threshold) */
   BD_ERR_HIP = 6,          /* a HIP runtime call failed */
-  BD_ERR_ALIGNMENT = 7     /* a bf16 tensor pointer is not 16-byte aligned */
+  BD_ERR_ALIGNMENT = 7,    /* a bf16 tensor pointer is not 16-byte aligned */
+  BD_ERR_SCRATCH = 8       /* the problem needs more scratch than the fixed buffer of a
+                              no-allocation entry point holds */
 } bd_status;
 
 typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
@@ -213,6 +216,32 @@ bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq
                                int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred,
                                int32_t* n_committed, int32_t* n_masked_left,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * bd_confidence_commit without a workspace argument and without any memory
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and errors as bd_confidence_commit.  The per-chunk
+ * partials that bd_confidence_commit keeps in the caller's workspace live here
+ * in a file-scope device array of BD_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held from the library's load until the process ends.  A shape whose
+ * bd_confidence_commit_workspace_size() exceeds it returns BD_ERR_SCRATCH
+ * (nothing is enqueued); 4 MiB covers every shape of at most 262144 rows
+ * (n_seq * blk_len), whatever the vocabulary.
+ *
+ * The array is not cleared between calls (each call writes every partial it
+ * reads).  All calls on one GPU share its array: two calls that may overlap in
+ * time on the same GPU (different streams, or different host threads without
+ * ordering) race on it and must be serialised by the caller.  The calling
+ * thread's current device must be the device of `stream`; the array's device
+ * address is looked up (hipGetSymbolAddress) on the first call per device.
+ * ---------------------------------------------------------------------- */
+#define BD_NOALLOC_SCRATCH_BYTES (4u << 20)
+bd_status bd_confidence_commit_noalloc(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
+                                       bd_dtype dtype, float threshold, bd_fallback fallback,
+                                       int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred,
+                                       int32_t* n_committed, int32_t* n_masked_left, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Confidence commit with a threshold per position (digest, weaknesses,

@@ -22,14 +22,14 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L.lib, n), n
     assert set(names) == set(L.EXPORTS)
 
 
 def test_status_strings_and_version():
-    for s in range(8):
+    for s in range(9):
         assert L.lib.bd_status_string(s)
     assert L.lib.bd_status_string(99) == b"unknown status"
     assert L.lib.bd_version() >= 100
@@ -230,3 +230,27 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 32, 1, 64)
     with pytest.raises(ValueError):
         bd.bd_attn_fwd(x, x, x)
+
+
+def test_commit_noalloc_validation():
+    """The no-allocation commit validates like bd_confidence_commit and refuses, before touching
+    the device, a shape whose partials exceed its fixed scratch (BD_NOALLOC_SCRATCH_BYTES)."""
+    def call(logits=FAKE, n_seq=1, blk=32, V=151936, dt=L.BD_BF16, T=0.95, fb=1, tok=FAKE, msk=FAKE):
+        return L.lib.bd_confidence_commit_noalloc(logits, V, n_seq, blk, V, dt, T, fb, tok, msk, None, None, None,
+                                                  None, None)
+    assert call(logits=None) == L.BD_ERR_NULL
+    assert call(tok=None) == L.BD_ERR_NULL
+    assert call(n_seq=0) == L.BD_ERR_SHAPE
+    assert call(blk=2048) == L.BD_ERR_UNSUPPORTED
+    assert call(T=math.nan) == L.BD_ERR_VALUE
+    assert call(fb=5) == L.BD_ERR_VALUE
+    cap = L.BD_NOALLOC_SCRATCH_BYTES
+    # the largest shapes that fit: 262144 rows at any vocabulary (one chunk per row from 8192 rows
+    # on, fewer than 16384 partials below)
+    for n_seq, blk, V in ((262144, 1, 151936), (8192, 32, 151936), (1, 32, 151936), (255, 32, 2**31 - 1),
+                          (8191, 1, 10**9)):
+        assert L.lib.bd_confidence_commit_workspace_size(n_seq, blk, V) <= cap, (n_seq, blk, V)
+    assert L.lib.bd_confidence_commit_workspace_size(262145, 1, 151936) > cap
+    assert call(n_seq=262145, blk=1) == L.BD_ERR_SCRATCH
+    assert call(n_seq=8193, blk=32) == L.BD_ERR_SCRATCH
+    assert L.lib.bd_status_string(L.BD_ERR_SCRATCH) != L.lib.bd_status_string(L.BD_ERR_WORKSPACE)
