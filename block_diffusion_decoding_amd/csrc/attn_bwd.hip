@@ -8,8 +8,9 @@
 // i sees key j iff floor(j / L') <= floor(i / L').
 //
 // Three kernels, no atomics (bit-for-bit deterministic):
-//   bwd_prep  per (batch, head, row): D = rowsum(dO * O) and LSE * log2(e),
-//             stored interleaved in the workspace.
+//   bwd_prep  per (batch, head, row): -D = -rowsum(dO * O) and -LSE / scale,
+//             two arrays [B, Hq, Lp] (rows padded to a multiple of 64 with
+//             zeros), the starting values of the dP and S accumulators.
 //   bwd_dkdv  workgroup = 4 waves = 128 consecutive keys of one (batch, kv
 //             head); each wave owns 32 keys with K and V in registers and walks
 //             the query tiles (64 rows) of every query head of the group, from
@@ -42,14 +43,16 @@ constexpr int kTileBytes = 64 * D * 2;   // 16 KB: one 64-row bf16 tile
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *dO;
   const float* lse;
-  float2* dl;          // [B, Hq, L]: (D, LSE * log2 e)
+  float* negD;         // [B, Hq, Lp]: -D = -rowsum(dO * O); 0 in the padding rows
+  float* nlse;         // [B, Hq, Lp]: -LSE / scale; 0 in the padding rows
   uint16_t *dq, *dk, *dv;
-  int B, L, Hq, Hkv, G, blk;
+  int B, L, Lp, Hq, Hkv, G, blk;
   float scale, scale_log2;
 };
 
 // ---------------------------------------------------------------------------
-// 16 lanes per row, rows of [B, L, Hq] in memory order.
+// 16 lanes per row, rows of [B, L, Hq] in memory order.  The first
+// B * Hq * (Lp - L) threads also zero the padding rows.
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gt >> 4;
@@ -73,17 +76,78 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
     const int h = (int)(row % p.Hq);
     const int64_t bi = row / p.Hq;
     const int i = (int)(bi % p.L), b = (int)(bi / p.L);
-    const int64_t o = ((int64_t)b * p.Hq + h) * p.L + i;
-    p.dl[o] = make_float2(s, p.lse[o] * kLog2e);
+    const int64_t bh = (int64_t)b * p.Hq + h;
+    p.negD[bh * p.Lp + i] = -s;
+    p.nlse[bh * p.Lp + i] = -p.lse[bh * p.L + i] / p.scale;
+  }
+  const int pad = p.Lp - p.L;
+  if (gt < (int64_t)p.B * p.Hq * pad) {
+    const int64_t bh = gt / pad;
+    const int64_t o = bh * p.Lp + p.L + (gt - bh * pad);
+    p.negD[o] = 0.f;
+    p.nlse[o] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
 // dK / dV
-constexpr int kKvNW = 4;                       // waves per workgroup (32 keys each)
+//
+// Workgroup = 8 waves = 4 pairs; pair g owns keys k0 + 32 g .. + 31 of one
+// (batch, kv head) and walks the 64-row query tiles of every query head of the
+// group from the first query that can see the workgroup's keys.  The two waves
+// of a pair sit on one SIMD and split the work by kind:
+//   score wave     K and V of the pair's keys in registers;
+//                  S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, sigma32
+//                  order; the accumulators start from -LSE/scale and -D of
+//                  their query rows, so they end as S - LSE/scale, dP - D), then
+//                  P = exp2((S - LSE/scale) scale log2 e), dS = P (dP - D) on
+//                  the vector ALU, packed to bf16;
+//   gradient wave  dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T by transposed
+//                  LDS reads, B = P / dS as the score wave packed them, read
+//                  from an LDS exchange area), the dK / dV accumulators; it
+//                  also issues the tile loads.
+// Every tile takes two phases ended by workgroup barriers:
+//   phase A(t)  score: store P / dS of tile t-1 to the exchange area, then the
+//                      products of tile t;
+//               gradient: issue the loads of tile t+1 (global -> LDS);
+//   phase B(t)  score: the vector work of tile t (P / dS kept in registers);
+//               gradient: the products of tile t-1, then wait for its loads.
+// So the vector work of one wave overlaps the products of the other on the
+// same SIMD, and products never wait on memory.  Ring stages: tile t+1 goes to
+// the stage of tile t-2, whose last reads (the gradient products of t-2) ended
+// in B(t-1).  (Measured alternatives: a double exchange area with half of the
+// gradient products moved into phase A, 15-20 % slower; reading further ahead
+// than four products, no change.)
+constexpr int kKvNW = 8;                       // waves per workgroup
+constexpr int kKvPairs = kKvNW / 2;            // 32 keys each
+constexpr int kKvKeys = 32 * kKvPairs;         // keys per workgroup
 constexpr int kKvNS = 3;                       // ring depth (query tiles)
-constexpr int kKvStage = 2 * kTileBytes + 512; // Q tile, dO tile, 64 x (D, LSE*log2e)
-constexpr size_t kDkdvSmem = (size_t)kKvNS * kKvStage;
+// LDS: the Q tiles of the three stages, then their dO tiles, then their
+// slices of -D and -LSE/scale (64 floats each), then the exchange areas of the
+// pairs and the SIMD ids.  Every read is a per-lane base register plus an
+// immediate offset below 64 KB (stage, slice and step are compile-time
+// constants).
+constexpr uint32_t kQRing = 0;
+constexpr uint32_t kDORing = kQRing + kKvNS * kTileBytes;
+constexpr uint32_t kDLRing = kDORing + kKvNS * kTileBytes;
+constexpr uint32_t kXchOff = kDLRing + kKvNS * 512;
+constexpr uint32_t kXchPair = 8 * 64 * 16;     // 8 operands of 16 bytes per lane
+constexpr uint32_t kKvIdsOff = kXchOff + kKvPairs * kXchPair;
+constexpr size_t kDkdvSmem = kKvIdsOff + 64;
+
+// Products whose LDS operands are read ahead (a tuning knob of the build).
+#ifndef BD_BWD_LOOK
+#define BD_BWD_LOOK 4
+#endif
+
+template <int S>
+using Stage = std::integral_constant<int, S>;
+
+// Hide how a per-lane LDS base was derived, so that the compiler keeps it as
+// its own register and every read from it fits the 16-bit offset field
+// (otherwise it rebuilds it from another base plus an offset above 64 KB,
+// one extra add per read).
+__device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -93,141 +157,260 @@ __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int L = p.L;
-  const int nkt = (L + 32 * kKvNW - 1) / (32 * kKvNW);
+  const int nkt = (L + kKvKeys - 1) / kKvKeys;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = wid % nkt;
   const int bk = wid / nkt;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-  const int k0 = kt * 32 * kKvNW;
-  const int kw0 = k0 + 32 * wave;          // this wave's first key
+  const int k0 = kt * kKvKeys;
+
+  // Pairs: the two waves the hardware placed on one SIMD (HW_ID bits 5:4),
+  // the first (by wave index) the score wave.  Otherwise waves 0-3 score and
+  // 4-7 compute gradients, pair = wave % 4; the pairing only affects speed.
+  const int simd = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* simd_of = reinterpret_cast<lds_int*>((uintptr_t)(lds0 + kKvIdsOff));
+  if (lane == 0) simd_of[wave] = simd;
+  __syncthreads();
+  int ids[kKvNW];
+#pragma unroll
+  for (int w = 0; w < kKvNW; ++w) ids[w] = __builtin_amdgcn_readfirstlane(simd_of[w]);
+  bool paired = true;
+  int rank = 0;
+#pragma unroll
+  for (int w = 0; w < kKvNW; ++w) {
+    int same = 0;
+#pragma unroll
+    for (int x = 0; x < kKvNW; ++x) same += (ids[x] == ids[w]);
+    paired = paired && same == 2;
+    rank += (w < wave && ids[w] == simd);
+  }
+  const bool scorer = __builtin_amdgcn_readfirstlane(paired ? rank == 0 : wave < kKvPairs);
+  const int gp = __builtin_amdgcn_readfirstlane(paired ? simd : (wave & (kKvPairs - 1)));
+
+  const int kw0 = k0 + 32 * gp;            // the pair's first key
   const int key = kw0 + col;               // this lane's key (B-operand column)
   const int qmin_key = (min(key, L - 1) / p.blk) * p.blk;   // first query that sees `key`
-  const int qmin_w = (min(kw0, L - 1) / p.blk) * p.blk;     // first query that sees any wave key
+  const int qmin_w = (min(kw0, L - 1) / p.blk) * p.blk;     // first query that sees any of the pair's keys
   const int qmin_w_hi = (min(kw0 + 31, L - 1) / p.blk) * p.blk;
   const int q_first = ((min(k0, L - 1) / p.blk) * p.blk / 64) * 64;
   const int nqt = (L - q_first + 63) / 64;
   const int n_iter = p.G * nqt;
-  const bool wave_live = kw0 < L;
-
+  const bool pair_live = kw0 < L;
   const int64_t kv_rs = (int64_t)p.Hkv * D, q_rs = (int64_t)p.Hq * D;
 
-  // this wave's share of iteration `it`'s tiles: Q, dO rows and the (D, LSE) slice
-  auto issue = [&](int it) {
-    const uint32_t st = lds0 + (uint32_t)(it % kKvNS) * kKvStage;
+  auto tile_q0 = [&](int it) __attribute__((always_inline)) { return q_first + (it % nqt) * 64; };
+  // a tile some query of which sees the pair's keys (the same test in both waves of the pair)
+  auto live = [&](int it) __attribute__((always_inline)) { return pair_live && tile_q0(it) + 64 > qmin_w; };
+
+  uint32_t xch = lds0 + kXchOff + gp * kXchPair + lane * 16;   // + 1024 * operand
+  opaque(xch);
+  const float c2 = p.scale_log2;
+
+  if (scorer) {
+    // ------------------------------------------------------------ score wave
+    bf16x8 kreg[8], vreg[8];
+    {
+      const int64_t off = ((int64_t)b * L + min(key, L - 1)) * kv_rs + (int64_t)kvh * D + 8 * half;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        kreg[t] = as_bf16x8(key < L ? ldg16(p.k + off + 16 * t) : make_uint4(0, 0, 0, 0));
+        vreg[t] = as_bf16x8(key < L ? ldg16(p.v + off + 16 * t) : make_uint4(0, 0, 0, 0));
+      }
+    }
+    vm_wait<0>();
+    __syncthreads();   // the gradient waves' loads of tile 0 are complete
+
+    // A-operand rows of Q / dO in sigma32 order (logical chunk 2*ds + half),
+    // stage 0; the -D / -LSE/scale slots of this lane's first query row.
+    uint32_t rq[8], rdo[8];
+    {
+      const int rrow = sigma32(col);
+      const int rswz = tile_swz(rrow);
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+        rq[ds] = lds0 + kQRing + rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
+        rdo[ds] = rq[ds] - kQRing + kDORing;
+        opaque(rdo[ds]);
+      }
+    }
+    uint32_t dl_lane = lds0 + kDLRing + 4 * 8 * half;   // + 256 for -LSE/scale
+    opaque(dl_lane);
+    f32x16 acc[4];      // S of slices 0, 1 and dP of slices 0, 1: acc[2 * which + qs]
+    bf16x8 pk[8];       // P / dS of the last tile: operand 4 qs + 2 kind + j (k-step 2 qs + j)
+
+    // Products of a tile in stage S: step i multiplies d-step i/4 of slice
+    // (i/2)%2, S (i even) or dP (i odd), so each accumulator recurs every 4
+    // products; each step's operand row is read kLook steps ahead.  The
+    // accumulators start from -LSE/scale (S) and -D (dP) of their query rows:
+    // entry i of slice qs is query 32 qs + 16 (i/8) + 8 half + (i%8), so each
+    // starting value is four 16-byte reads of the tile's slices.
+    auto products = [&](auto sc) __attribute__((always_inline)) {
+      constexpr uint32_t so = decltype(sc)::value * kTileBytes;
+      constexpr uint32_t sl = decltype(sc)::value * 512;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int qs = a & 1;
+        const uint32_t base = dl_lane + sl + (a < 2 ? 256u : 0u) + 4 * 32 * qs;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (uintptr_t)(base + 4 * 16 * (r >> 1) + 16 * (r & 1)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a][4 * r + e] = w[e];
+        }
+      }
+      constexpr int kLook = BD_BWD_LOOK;
+      bf16x8 op[32];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        const int ds = i >> 2, qs = (i >> 1) & 1, which = i & 1;
+        op[i] = lds_read_b128((which ? rdo[ds] : rq[ds]) + so + 32 * qs * 256);
+      };
+#pragma unroll
+      for (int i = 0; i < kLook; ++i) rd(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16 + kLook, 0);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + kLook < 32) rd(i + kLook);
+        const int ds = i >> 2, qs = (i >> 1) & 1, which = i & 1;
+        acc[2 * which + qs] = mfma_32x32x16(op[i], which ? vreg[ds] : kreg[ds], acc[2 * which + qs]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kLook < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+
+    // Vector work of a tile: P = exp2((S - LSE/scale) scale log2 e),
+    // dS = P (dP - D).  Only tiles that reach below the pair's last key block or
+    // past the sequence end need the mask.
+    auto vector_work = [&](int it) __attribute__((always_inline)) {
+      const int q0 = tile_q0(it);
+      auto body = [&](auto masked_c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int i = 8 * j + e;
+              float pe = exp2_fast(acc[qs][i] * c2);
+              if (decltype(masked_c)::value) {
+                const int q = q0 + 32 * qs + 16 * j + 8 * half + e;
+                if (q < qmin_key || q >= L) pe = 0.f;
+              }
+              pv[e] = pe;
+              dsv[e] = pe * acc[2 + qs][i];
+            }
+            pk[4 * qs + j] = pack_bf16x8(pv);
+            pk[4 * qs + 2 + j] = pack_bf16x8(dsv);
+          }
+      };
+      if (q0 < qmin_w_hi || q0 + 64 > L) body(std::true_type());
+      else body(std::false_type());
+    };
+
+    // Tile t in stage S (= t % 3): phase A(t), phase B(t).
+    auto tile = [&](auto sc, int t) __attribute__((always_inline)) {
+      if (t >= 1 && live(t - 1)) {
+#pragma unroll
+        for (int o = 0; o < 8; ++o)
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>((uintptr_t)(xch + 1024 * o)) = pk[o];
+      }
+      if (t < n_iter && live(t)) products(sc);
+      __syncthreads();
+      if (t < n_iter && live(t)) vector_work(t);
+      __syncthreads();
+    };
+    for (int t = 0; t <= n_iter; t += 3) {
+      tile(Stage<0>(), t);
+      if (t + 1 <= n_iter) tile(Stage<1>(), t + 1);
+      if (t + 2 <= n_iter) tile(Stage<2>(), t + 2);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- gradient wave
+  // Loads of tile `it` into stage S: Q and dO rows (a quarter each) and the
+  // -D and -LSE/scale slices (64 floats each, rows q0 .. q0 + 63 of the padded
+  // arrays): lanes 0..15 of pair 0's wave copy four rows of -D each, lanes
+  // 16..31 four rows of -LSE/scale.
+  auto issue = [&](auto sc, int it) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
     const int hq = kvh * p.G + it / nqt;
-    const int q0 = q_first + (it % nqt) * 64;
+    const int q0 = tile_q0(it);
     const uint16_t* qb = p.q + (int64_t)b * L * q_rs + (int64_t)hq * D;
     const uint16_t* dob = p.dO + (int64_t)b * L * q_rs + (int64_t)hq * D;
-    tile_dma<kKvNW>(st, qb, q_rs, q0, L, wave, lane);
-    tile_dma<kKvNW>(st + kTileBytes, dob, q_rs, q0, L, wave, lane);
-    // 64 float2 = 512 bytes: lanes 0..31 of every wave copy the same slice, rows
-    // q0 + 2l and q0 + 2l + 1 to slots 2l, 2l + 1.  When only the first row of a
-    // pair exists, the second read runs 8 bytes into the next head's rows (or
-    // into the workspace's 16 bytes of slack); lanes wholly past the end read
-    // from row 0.  Query rows past the end are masked below.
-    const float2* dlb = p.dl + ((int64_t)b * p.Hq + hq) * L;
-    const int r2 = q0 + 2 * lane;
-    if (lane < 32) lds_dma16(dlb + (r2 < L ? r2 : 0), st + 2 * kTileBytes);
+    tile_dma<kKvPairs>(lds0 + kQRing + S * kTileBytes, qb, q_rs, q0, L, gp, lane);
+    tile_dma<kKvPairs>(lds0 + kDORing + S * kTileBytes, dob, q_rs, q0, L, gp, lane);
+    const int64_t bh = ((int64_t)b * p.Hq + hq) * p.Lp + q0;
+    if (gp == 0 && lane < 32)
+      lds_dma16((lane < 16 ? p.negD + bh + 4 * lane : p.nlse + bh + 4 * (lane - 16)), lds0 + kDLRing + S * 512);
   };
-  for (int u = 0; u < kKvNS - 1 && u < n_iter; ++u) issue(u);
 
-  bf16x8 kreg[8], vreg[8];
-  {
-    const int64_t off = ((int64_t)b * L + min(key, L - 1)) * kv_rs + (int64_t)kvh * D + 8 * half;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      kreg[t] = as_bf16x8(key < L ? ldg16(p.k + off + 16 * t) : make_uint4(0, 0, 0, 0));
-      vreg[t] = as_bf16x8(key < L ? ldg16(p.v + off + 16 * t) : make_uint4(0, 0, 0, 0));
-    }
-  }
+  if (n_iter > 0) issue(Stage<0>(), 0);
   vm_wait<0>();
+  __syncthreads();
 
   f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk_acc[db][i] = 0.f; dv_acc[db][i] = 0.f; }
-
-  // Per-lane LDS offsets within a stage: A-operand rows of Q / dO in sigma32
-  // order (logical chunk 2*ds + half), and the transposed-read addresses of Q^T /
-  // dO^T (as the forward's V^T reads).
-  uint32_t raddr[8], taddr[8];
-  {
-    const int rrow = sigma32(col);
-    const int rswz = tile_swz(rrow);
+  uint32_t tq[8], tdo[8];
+  tr32_bases(tq, lds0 + kQRing, lane);
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) raddr[ds] = rrow * 256 + (((2 * ds + half) ^ rswz) << 4);
-    tr32_bases(taddr, 0, lane);
+  for (int y = 0; y < 8; ++y) {
+    tdo[y] = tq[y] - kQRing + kDORing;
+    opaque(tdo[y]);
   }
-  const float c2 = p.scale_log2;
 
-  for (int it = 0; it < n_iter; ++it) {
-    {
-      const int pending = min(kKvNS - 2, n_iter - 1 - it);
-      constexpr int per = 2 * (16 / kKvNW) + 1;
-      if (pending >= 1) vm_wait<per>();
-      else vm_wait<0>();
+  // Products of the tile in stage S (k-step s = 16 query rows): step i takes
+  // k-step i/8, d-block (i/2)%4 and dV (i even) or dK (i odd), so each
+  // accumulator recurs every 8 products; A operands kLook steps ahead.
+  auto products = [&](auto sc) __attribute__((always_inline)) {
+    constexpr uint32_t so = decltype(sc)::value * kTileBytes;
+    bf16x8 bop[8];
+#pragma unroll
+    for (int o = 0; o < 8; ++o)
+      bop[o] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>((uintptr_t)(xch + 1024 * o));
+    constexpr int kLook = BD_BWD_LOOK;
+    bf16x8 op[32];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int s4 = i >> 3, db = (i >> 1) & 3, which = i & 1;
+      const uint32_t* t = which ? tq : tdo;    // dK: Q^T; dV: dO^T
+      op[i] = cat_i16x4(lds_read_tr16(t[tr32_idx(db, s4, 0)] + so + tr32_off(s4, 0)),
+                        lds_read_tr16(t[tr32_idx(db, s4, 1)] + so + tr32_off(s4, 1)));
+    };
+#pragma unroll
+    for (int i = 0; i < kLook; ++i) rd(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * kLook, 0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + kLook < 32) rd(i + kLook);
+      const int s4 = i >> 3, db = (i >> 1) & 3, which = i & 1;
+      // operand of k-step s4 = 2 qs + j: P at 4 qs + j, dS at 4 qs + 2 + j
+      const bf16x8& bb = bop[4 * (s4 >> 1) + 2 * which + (s4 & 1)];
+      if (which) dk_acc[db] = mfma_32x32x16(op[i], bb, dk_acc[db]);
+      else dv_acc[db] = mfma_32x32x16(op[i], bb, dv_acc[db]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kLook < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+  };
+
+  // Tile t: phase A(t) issues the loads of tile t+1 (stage (t+1) % 3), phase
+  // B(t) multiplies tile t-1 (stage (t+2) % 3) and waits for those loads.
+  auto tile = [&](auto sc, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    if (t + 1 < n_iter) issue(Stage<(S + 1) % kKvNS>(), t + 1);
     __syncthreads();
-    if (it + kKvNS - 1 < n_iter) issue(it + kKvNS - 1);
-    const int q0 = q_first + (it % nqt) * 64;
-    if (!wave_live || q0 + 64 <= qmin_w) continue;      // no query of the tile sees this wave's keys
-    const uint32_t st = lds0 + (uint32_t)(it % kKvNS) * kKvStage;
-    const uint32_t Qt = st, dOt = st + kTileBytes;
-    const float2* dl_s = reinterpret_cast<const float2*>(reinterpret_cast<const char*>(smem) + (st - lds0) + 2 * kTileBytes);
-    const bool partial = q0 < qmin_w_hi;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      if (q0 + 32 * qs + 32 <= qmin_w) continue;
-      f32x16 s_acc, dp_acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { s_acc[i] = 0.f; dp_acc[i] = 0.f; }
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        s_acc = mfma_32x32x16(lds_read_b128(Qt + 32 * qs * 256 + raddr[ds]), kreg[ds], s_acc);
-        dp_acc = mfma_32x32x16(lds_read_b128(dOt + 32 * qs * 256 + raddr[ds]), vreg[ds], dp_acc);
-      }
-      // entry i of this lane holds query q0 + 32*qs + 16*(i/8) + 8*half + (i%8)
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int qb0 = 32 * qs + 16 * j + 8 * half;
-        const float4* src = reinterpret_cast<const float4*>(dl_s + qb0);
-        float dd[8], ll[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float4 w = src[e];
-          dd[2 * e] = w.x; ll[2 * e] = w.y; dd[2 * e + 1] = w.z; ll[2 * e + 1] = w.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * j + e;
-          float pe = exp2_fast(__builtin_fmaf(s_acc[i], c2, -ll[e]));
-          if (partial && (q0 + qb0 + e) < qmin_key) pe = 0.f;
-          if (q0 + qb0 + e >= L) pe = 0.f;
-          pv[i] = pe;
-          dsv[i] = pe * (dp_acc[i] - dd[e]);
-        }
-      }
-      const bf16x8 pb0 = pack_bf16x8(pv), pb1 = pack_bf16x8(pv + 8);
-      const bf16x8 sb0 = pack_bf16x8(dsv), sb1 = pack_bf16x8(dsv + 8);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int s0 = 2 * qs;   // 16-row k-steps 2qs, 2qs+1 of the 64-row tile
-        const bf16x8 dto0 = cat_i16x4(lds_read_tr16(dOt + taddr[tr32_idx(db, s0, 0)] + tr32_off(s0, 0)),
-                                      lds_read_tr16(dOt + taddr[tr32_idx(db, s0, 1)] + tr32_off(s0, 1)));
-        const bf16x8 dto1 = cat_i16x4(lds_read_tr16(dOt + taddr[tr32_idx(db, s0 + 1, 0)] + tr32_off(s0 + 1, 0)),
-                                      lds_read_tr16(dOt + taddr[tr32_idx(db, s0 + 1, 1)] + tr32_off(s0 + 1, 1)));
-        dv_acc[db] = mfma_32x32x16(dto0, pb0, dv_acc[db]);
-        dv_acc[db] = mfma_32x32x16(dto1, pb1, dv_acc[db]);
-        const bf16x8 qt0 = cat_i16x4(lds_read_tr16(Qt + taddr[tr32_idx(db, s0, 0)] + tr32_off(s0, 0)),
-                                     lds_read_tr16(Qt + taddr[tr32_idx(db, s0, 1)] + tr32_off(s0, 1)));
-        const bf16x8 qt1 = cat_i16x4(lds_read_tr16(Qt + taddr[tr32_idx(db, s0 + 1, 0)] + tr32_off(s0 + 1, 0)),
-                                     lds_read_tr16(Qt + taddr[tr32_idx(db, s0 + 1, 1)] + tr32_off(s0 + 1, 1)));
-        dk_acc[db] = mfma_32x32x16(qt0, sb0, dk_acc[db]);
-        dk_acc[db] = mfma_32x32x16(qt1, sb1, dk_acc[db]);
-      }
-    }
+    if (t >= 1 && live(t - 1)) products(Stage<(S + 2) % kKvNS>());
+    vm_wait<0>();
+    __syncthreads();
+  };
+  for (int t = 0; t <= n_iter; t += 3) {
+    tile(Stage<0>(), t);
+    if (t + 1 <= n_iter) tile(Stage<1>(), t + 1);
+    if (t + 2 <= n_iter) tile(Stage<2>(), t + 2);
   }
 
   if (key >= L) return;
@@ -296,8 +479,8 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
       doreg[t] = as_bf16x8(qrow < L ? ldg16(p.dO + off + 16 * t) : make_uint4(0, 0, 0, 0));
     }
   }
-  const float2 dl = p.dl[((int64_t)b * p.Hq + hq) * L + min(qrow, L - 1)];
-  const float Dq = dl.x, nlse2 = -dl.y;
+  const int64_t bhq = ((int64_t)b * p.Hq + hq) * p.Lp + min(qrow, L - 1);
+  const float Dq = -p.negD[bhq], nlse2 = p.nlse[bhq] * p.scale_log2;
   vm_wait<0>();
 
   f32x16 acc[4];
@@ -380,7 +563,8 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int batch, int seqlen, int n_q_heads) {
-  return (size_t)batch * n_q_heads * seqlen * sizeof(float2) + 16;
+  const size_t lp = ((size_t)seqlen + 63) / 64 * 64;
+  return 2 * (size_t)batch * n_q_heads * lp * sizeof(float) + 16;
 }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -403,7 +587,9 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.o = static_cast<const uint16_t*>(o);
   p.dO = static_cast<const uint16_t*>(d_o);
   p.lse = lse;
-  p.dl = static_cast<float2*>(ws);
+  p.Lp = (s.seqlen + 63) / 64 * 64;
+  p.negD = static_cast<float*>(ws);
+  p.nlse = p.negD + (size_t)s.batch * s.n_q_heads * p.Lp;
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
@@ -416,10 +602,12 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.scale = s.scale;
   p.scale_log2 = s.scale * kLog2e;
   const long long rows = (long long)s.batch * s.seqlen * s.n_q_heads;
-  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, p);
+  const long long pad = (long long)s.batch * s.n_q_heads * (p.Lp - s.seqlen);
+  const long long prep_threads = rows * 16 > pad ? rows * 16 : pad;
+  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + 32 * kKvNW - 1) / (32 * kKvNW));
+  const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + kKvKeys - 1) / kKvKeys);
   hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)nk), dim3(kKvNW * 64), kDkdvSmem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
