@@ -451,6 +451,13 @@ def main():
         if rnd:
             com1_us.extend(t_us)
     dec1_us, com1_us = np.array(dec1_us), np.array(com1_us)
+    # floor of a call that launches two kernels: two empty kernels back to back, timed the same way
+    floor_us = []
+    for rnd in range(4):
+        t_us = primed([lambda: (torch.cuda._sleep(0), torch.cuda._sleep(0)) for _ in range(n_copies_lg)])
+        if rnd:
+            floor_us.extend(t_us)
+    floor_us = np.array(floor_us)
     dec1_bytes = (sw.prefix_len + sw.block_size) * Hkv * D * 2 * 2
     com1_bytes = sw.block_size * sw.vocab * 2
 
@@ -580,6 +587,9 @@ def main():
                         "commit_sampled_topp0.9_GBps_first_step":
                             round(rw_bytes / (np.median(tr_us[(0, 0.9)]) * 1e-6) / 1e9, 1),
                         "by_threshold": loops, "by_threshold_graph_replay": loops_graph},
+        "launch_floor_two_empty_kernels_us": {"us_median": round(float(np.median(floor_us)), 2),
+                                              "us_p10": round(float(np.percentile(floor_us, 10)), 2),
+                                              "us_p90": round(float(np.percentile(floor_us, 90)), 2)},
         "decode_step_4096": {"bytes": dec1_bytes, "us_median": round(float(np.median(dec1_us)), 2),
                              "us_p10": round(float(np.percentile(dec1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(dec1_us, 90)), 2),

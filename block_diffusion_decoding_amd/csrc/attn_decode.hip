@@ -75,7 +75,13 @@ __device__ __forceinline__ void lds_write16(uint32_t lds_addr, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)lds_addr) = w;
 }
-constexpr int kMinRangeTiles = 8;             // fewest tiles per range the plan aims for
+#ifndef BD_DECODE_MIN_RANGE
+#define BD_DECODE_MIN_RANGE 8
+#endif
+#ifndef BD_DECODE_MERGE_BATCH
+#define BD_DECODE_MERGE_BATCH 8
+#endif
+constexpr int kMinRangeTiles = BD_DECODE_MIN_RANGE;   // fewest tiles per range the plan aims for
 
 struct DecParams {
   const uint16_t* q_blk;
@@ -568,7 +574,7 @@ __global__ __launch_bounds__(256) void decode_merge(DecParams p) {
   if (r_first == r_last || row >= p.rows) return;
 
   // partials in batches of kBatch per round trip to memory
-  constexpr int kBatch = 8;
+  constexpr int kBatch = BD_DECODE_MERGE_BATCH;
   float m = kNegInf, lsum = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
