@@ -391,9 +391,12 @@ __global__ __launch_bounds__(kThreads) void sample_locate(const T* __restrict__ 
         }
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(k0 + lane < nchunk && before + incl > target);
         if (hit) {
+          // the chunks before the crossing one sum to lane l-1's inclusive value, the
+          // very sum the crossing test found not to pass the target: target - before >= 0
           const int l = __builtin_ctzll(hit);
           chunk = k0 + l;
-          before += __shfl(incl, l, 64) - __shfl(v, l, 64);
+          const float excl = __shfl(incl, l > 0 ? l - 1 : 0, 64);
+          if (l > 0) before += excl;
           found = true;
         } else {
           before += __shfl(incl, 63, 64);
@@ -447,19 +450,25 @@ __global__ __launch_bounds__(kThreads) void sample_locate(const T* __restrict__ 
     sum += q;
     last_pos = q > 0.f ? v : last_pos;
   }
-  // exclusive scan of the slice sums (thread order = id order)
+  // scan of the slice sums (thread order = id order); each thread's interval
+  // [lower, upper) takes its ends from the same sums as its neighbours', so the
+  // intervals tile the chunk without gaps and exactly one brackets a target
+  // below the chunk total
   float incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float y = __shfl_up(incl, off, 64);
     if (lane >= off) incl += y;
   }
+  float prev = __shfl_up(incl, 1, 64);
+  if (lane == 0) prev = 0.f;
   if (lane == 63) s_wsum[wave] = incl;
   atomicMax(&s_last, last_pos);
   __syncthreads();
-  float pre = incl - sum;
-  for (int w = 0; w < wave; ++w) pre += s_wsum[w];
-  if (pre <= res && res < pre + sum) {
+  float wbase = 0.f;
+  for (int w = 0; w < wave; ++w) wbase += s_wsum[w];
+  const float pre = wbase + prev, upper = wbase + incl;
+  if (pre <= res && res < upper) {
     // Rescan the slice in id order for the first running sum past the target:
     // whole vectors four loads at a time (the slice was just read: cache hits),
     // the running sum kept per vector, then the elements of the crossing vector.
@@ -1095,11 +1104,14 @@ __global__ __launch_bounds__(kTrThreads) void sample_truncated(const T* __restri
   }
   __syncthreads();
   if (tr_uni(sh.id) < 0) {
-    // rounding left no vector or thread past the target: the last kept id
+    // rounding left no thread of vector js past the target: the last kept id of
+    // that vector (the target lies at its end); with no vector past it, the
+    // last kept id of the row
     int last = -1;
 #pragma unroll
     for (int j = 0; j < kTrVec; ++j) {
       tr_fence(r[j]);
+      if (js >= 0 && j != js) continue;
 #pragma unroll
       for (int e = 0; e < N; ++e) last = E::key(r[j], e) >= cut_key ? (j * kTrThreads + tid) * N + e : last;
     }

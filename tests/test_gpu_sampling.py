@@ -148,3 +148,38 @@ def test_reproducible_and_fresh_per_step():
     a, b, d = draw(4), draw(4), draw(5)
     assert np.array_equal(a, b)
     assert (a != d).mean() > 0.5
+
+
+def test_target_on_a_chunk_boundary():
+    """A draw that lands on the boundary between two vocabulary chunks of the reduce.  1024 rows
+    hold one logit row of 65536 ids (chunks of 4096 ids per row with the default chunking); the
+    generator's steps are searched (oracle Philox4x32-10) for a row whose u lies within 5e-7 of
+    the cumulative probability at a chunk boundary, where each id carries ~1.5e-5.  The sampled id
+    must be one of the two ids at that boundary (rounding may pick either side, never an id far
+    from it), and the whole step passes the usual sampling grade."""
+    banner("sampled commit: target on a chunk boundary")
+    rng = np.random.default_rng(31)
+    V, chunk, n_seq, blk = 65536, 4096, 32, 32
+    bits = W.f32_to_bf16_bits(rng.uniform(-1.0, 1.0, V).astype(np.float32))
+    x = W.bf16_bits_to_f32(bits).astype(np.float64)
+    p = np.exp(x - x.max())
+    cum = np.cumsum(p / p.sum())
+    bounds = cum[np.arange(1, V // chunk) * chunk - 1]     # probability of ids below each boundary
+    seed, found = 91, None
+    for step in range(4000):
+        for r in range(n_seq * blk):
+            u = S.row_uniform(seed, r, step)
+            k = int(np.argmin(np.abs(bounds - u)))
+            if abs(bounds[k] - u) < 5e-7:
+                found = (step, r, (k + 1) * chunk)
+                break
+        if found:
+            break
+    assert found, "no draw near a boundary"
+    step, r, b_id = found
+    rows = np.repeat(bits[None], n_seq * blk, axis=0)
+    masked = np.ones(n_seq * blk, np.uint8)
+    tokens = np.full(n_seq * blk, -1, np.int32)
+    gpu, ref = run_case(rows, "bf16", tokens, masked, blk, 2.0, 1.0, seed, step, fallback=False)
+    print(f"  step {step} row {r}: boundary before id {b_id}, oracle id {ref['pred'][r]}, GPU id {gpu['pred'][r]}")
+    assert gpu["pred"][r] in (b_id - 1, b_id), (gpu["pred"][r], b_id)
