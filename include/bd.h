@@ -126,7 +126,9 @@ bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o
  *        may be NULL only if every prefix_len is 0)
  *   prefix_start int64[n_seq], prefix_len int32[n_seq]  in, DEVICE memory;
  *        prefix_len[s] must lie in [0, max_prefix_len]
- *   max_prefix_len  host value, an upper bound of prefix_len (sizes the grid)
+ *   max_prefix_len  host value, an upper bound of prefix_len (sizes the grid;
+ *        with this packed cache a larger prefix_len still gives the exact
+ *        result, only the split of the work is then unbalanced)
  *   o [n_seq, blk_len, n_q_heads, head_dim]        out
  *   lse [n_seq, n_q_heads, blk_len] float32        out, may be NULL
  *   workspace of bd_attn_decode_workspace_size() bytes (split-KV partial

@@ -171,6 +171,17 @@ def test_decode_ragged(plens, T, Hq, Hkv):
     check_decode(d, "bf16", o2, lse2)
 
 
+@pytest.mark.parametrize("plens,max_p", [
+    ([600, 50], 40),                 # split planned for 6 tiles, 23 run
+    ([2000, 5, 900, 70, 900, 3, 900, 900, 0, 900], 900),   # one sequence past the bound
+])
+def test_decode_prefix_above_bound(plens, max_p):
+    banner(f"decode bf16 plens={plens} max_prefix_len={max_p}")
+    d = W.decode_inputs(len(plens), plens, 32, 16, 8, 128, "bf16", seed=sum(plens) + max_p)
+    o, lse = gpu_decode(d, "bf16", max_p)
+    check_decode(d, "bf16", o, lse)
+
+
 def test_decode_matches_forward_rows():
     """Decoding block b against the first b blocks as a cache equals the forward rows of block b."""
     banner("decode bf16 == forward rows")
