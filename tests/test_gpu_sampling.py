@@ -95,14 +95,18 @@ def test_invalid_rows_and_neg_inf():
         assert gpu["pred"][4] % 2 == 1 and gpu["pred"][3] >= 2500
 
 
-def test_batched_loop_scale():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_batched_loop_scale(dtype):
+    """64 x 32 rows of 151936 ids, bf16 and fp32 (the same values): the full-size step, with the
+    target's chunk of 10240 ids rescanned as 5 vectors of 8 or 10 vectors of 4 per thread."""
     wl = W.WORKLOADS["decode_loop_bf16"]
-    banner("sampled commit 64 x 32 x 151936")
+    banner(f"sampled commit 64 x 32 x 151936 {dtype}")
     rng = np.random.default_rng(wl.seed)
     bits = W.boosted_logits_bits(64 * 32, wl.vocab, wl.boost[0], wl.boost[1], rng)
     masked = (rng.random(64 * 32) < 0.6).astype(np.uint8)
     tokens = np.where(masked == 1, -1, 5).astype(np.int32)
-    run_case(bits, "bf16", tokens, masked, 32, 0.95, 1.0, seed=21, step=3)
+    logits = bits if dtype == "bf16" else W.bf16_bits_to_f32(bits)
+    run_case(logits, dtype, tokens, masked, 32, 0.95, 1.0, seed=21, step=3)
 
 
 def test_sample_frequencies_match_the_distribution():
