@@ -5,8 +5,10 @@
 #include "bd.h"
 #include "bd_kernels.hpp"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 namespace {
 
@@ -22,6 +24,33 @@ bd_status hip_status(hipError_t e) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The product of non-negative sizes exceeds limit (>= 0), found without
+// overflow: while the running product is at most limit, one more factor up to
+// INT_MAX keeps it below 2^62.
+bool exceeds(long long limit, std::initializer_list<long long> factors) {
+  long long p = 1;
+  for (const long long f : factors) {
+    if (f != 0 && p > limit / f) return true;
+    p *= f;
+  }
+  return p > limit;
+}
+
+// Sizes of an attention call: positive, whole query-head groups, and a grid
+// that fits (one workgroup per (batch, head, row tile) at most).
+bool attn_sizes_ok(int batch, int seqlen, int hq, int hkv) {
+  if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+  return !exceeds(kMaxGrid, {batch, hq, seqlen});
+}
+
+// Rows of a commit call, and its reduce grid, that fit.
+bool commit_rows_ok(int n_seq, int blk_len, int vocab) {
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || vocab > BD_MAX_VOCAB || blk_len > bd::kCommitMaxBlock)
+    return false;
+  const long long rows = (long long)n_seq * blk_len;
+  return !exceeds(kMaxGrid, {rows, bd::commit_chunks_per_row(rows, vocab)});
+}
+
 float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
 
 bd_status check_attn_shape(int batch, int seqlen, int hq, int hkv, int d, int blk, bd_dtype dtype, float scale) {
@@ -35,7 +64,7 @@ bd_status check_attn_shape(int batch, int seqlen, int hq, int hkv, int d, int bl
   } else {
     return BD_ERR_UNSUPPORTED;
   }
-  if ((long long)batch * hq * seqlen > kMaxGrid) return BD_ERR_SHAPE;
+  if (!attn_sizes_ok(batch, seqlen, hq, hkv)) return BD_ERR_SHAPE;
   return BD_OK;
 }
 
@@ -49,8 +78,7 @@ bd_status commit_common(const void* logits, int64_t row_stride, int n_seq, int b
   if (dtype != BD_F32 && dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
   if (std::isnan(threshold)) return BD_ERR_VALUE;
   if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
-  const long long rows = (long long)n_seq * blk_len;
-  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
+  if (!commit_rows_ok(n_seq, blk_len, vocab)) return BD_ERR_SHAPE;
   const size_t need = bd::commit_workspace_bytes(n_seq, blk_len, vocab);
   if (noalloc) {
     if (need > bd::kNoAllocScratchBytes) return BD_ERR_SCRATCH;
@@ -105,9 +133,7 @@ bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
 }
 
 size_t bd_attn_bwd_workspace_size(int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim) {
-  (void)n_kv_heads;
-  (void)head_dim;
-  if (batch <= 0 || seqlen <= 0 || n_q_heads <= 0) return 0;
+  if (head_dim <= 0 || !attn_sizes_ok(batch, seqlen, n_q_heads, n_kv_heads)) return 0;
   return bd::attn_bwd_workspace_bytes(batch, seqlen, n_q_heads);
 }
 
@@ -138,8 +164,8 @@ bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o
 
 size_t bd_attn_decode_workspace_size(int n_seq, int blk_len, int max_prefix_len, int n_q_heads, int n_kv_heads,
                                      int head_dim) {
-  if (n_seq <= 0 || blk_len <= 0 || max_prefix_len < 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
-      n_q_heads % n_kv_heads != 0 || head_dim <= 0)
+  if (max_prefix_len < 0 || head_dim <= 0 || !attn_sizes_ok(n_seq, blk_len, n_q_heads, n_kv_heads) ||
+      (long long)max_prefix_len + blk_len > kMaxGrid / 2)
     return 0;
   bd::DecodeShape s{n_seq, blk_len, max_prefix_len, n_q_heads, n_kv_heads, head_dim, 1.f};
   return bd::decode_workspace_bytes(s, 1);
@@ -207,6 +233,9 @@ bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages
   if (!k_blk || !v_blk || !k_pages || !v_pages || !block_table || !prefix_len) return BD_ERR_NULL;
   if (n_seq <= 0 || blk_len <= 0 || n_kv_heads <= 0 || head_dim <= 0 || max_pages_per_seq <= 0) return BD_ERR_SHAPE;
   if (page_size <= 0) return BD_ERR_SHAPE;
+  // a row's elements, and the block's 16-byte pieces, are counted in int
+  if (exceeds(INT_MAX, {n_kv_heads, head_dim}) || exceeds(8LL * INT_MAX, {blk_len, n_kv_heads, head_dim}))
+    return BD_ERR_SHAPE;
   if (dtype != BD_BF16) return BD_ERR_UNSUPPORTED;
   if ((n_kv_heads * head_dim) % 8 != 0) return BD_ERR_UNSUPPORTED;
   if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pages) || !aligned16(v_pages)) return BD_ERR_ALIGNMENT;
@@ -216,7 +245,7 @@ bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages
 }
 
 size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab) {
-  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  if (!commit_rows_ok(n_seq, blk_len, vocab)) return 0;
   return bd::commit_workspace_bytes(n_seq, blk_len, vocab);
 }
 
@@ -247,7 +276,7 @@ bd_status bd_confidence_commit_rowwise(const void* logits, int64_t row_stride, i
 }
 
 size_t bd_confidence_commit_sampled_workspace_size(int n_seq, int blk_len, int vocab) {
-  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  if (!commit_rows_ok(n_seq, blk_len, vocab)) return 0;
   return bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
 }
 
@@ -267,8 +296,7 @@ bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, i
   if (fallback != BD_FALLBACK_NONE && fallback != BD_FALLBACK_TOP1) return BD_ERR_VALUE;
   const bool truncate = top_k > 0 || top_p < 1.f;
   if (truncate && vocab > bd::sample_truncated_max_vocab(dtype == BD_BF16)) return BD_ERR_UNSUPPORTED;
-  const long long rows = (long long)n_seq * blk_len;
-  if (rows * bd::commit_chunks_per_row(rows, vocab) > kMaxGrid) return BD_ERR_SHAPE;
+  if (!commit_rows_ok(n_seq, blk_len, vocab)) return BD_ERR_SHAPE;
   const size_t need = bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, nullptr,
@@ -279,7 +307,8 @@ bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, i
 }
 
 size_t bd_lmhead_commit_workspace_size(int n_seq, int blk_len, int vocab) {
-  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0) return 0;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || vocab > BD_MAX_VOCAB || blk_len > bd::kCommitMaxBlock) return 0;
+  if ((long long)n_seq * blk_len > kMaxGrid / 256) return 0;
   return bd::lmhead_workspace_bytes(n_seq, blk_len);
 }
 
@@ -288,7 +317,7 @@ bd_status bd_lmhead_commit(const void* hidden, int64_t hidden_stride, const void
                            int32_t* tokens, uint8_t* masked, float* conf, int32_t* pred, int32_t* n_committed,
                            int32_t* n_masked_left, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!hidden || !weight || !tokens || !masked) return BD_ERR_NULL;
-  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || hidden_dim <= 0) return BD_ERR_SHAPE;
+  if (n_seq <= 0 || blk_len <= 0 || vocab <= 0 || vocab > BD_MAX_VOCAB || hidden_dim <= 0) return BD_ERR_SHAPE;
   if (hidden_stride < hidden_dim || weight_stride < hidden_dim) return BD_ERR_SHAPE;
   if (blk_len > bd::kCommitMaxBlock) return BD_ERR_UNSUPPORTED;
   if (hidden_dim % 64 != 0 || hidden_dim > bd::lmhead_max_hidden()) return BD_ERR_UNSUPPORTED;

@@ -294,11 +294,13 @@ __global__ __launch_bounds__(kThr) void commit_decide(const Partial* __restrict_
 // Vocabulary entries per chunk for rows x vocab logits: about kTargetWGs
 // workgroups in all, chunks of at least kMinChunk entries, a multiple of
 // kStep (so that every chunk but a row's last starts and ends on whole steps).
+// Computed in 64 bits: for vocabularies up to 2^30 the length fits an int.
 int commit_chunk_len(long long rows, int vocab, long long target_wgs = kTargetWGs) {
+  const long long v = vocab;
   const long long want = std::max<long long>(1, (target_wgs + rows - 1) / rows);
-  const long long most = std::max<long long>(1, (vocab + kMinChunk - 1) / kMinChunk);
+  const long long most = std::max<long long>(1, (v + kMinChunk - 1) / kMinChunk);
   const long long nchunk = std::min(want, most);
-  const long long len = (vocab + nchunk - 1) / nchunk;
+  const long long len = (v + nchunk - 1) / nchunk;
   return (int)(((len + kStep - 1) / kStep) * kStep);
 }
 
@@ -1151,14 +1153,14 @@ hipError_t launch_decide(const void* part, int nchunk, const float* row_conf, co
 size_t commit_sampled_workspace_bytes(int n_seq, int blk_len, int vocab) {
   const long long rows = (long long)n_seq * blk_len;
   const int len = commit_chunk_len(rows, vocab, kSampleTargetWGs);
-  return (size_t)rows * ((vocab + len - 1) / len) * sizeof(Partial) + (size_t)rows * 8;
+  return (size_t)rows * (((long long)vocab + len - 1) / len) * sizeof(Partial) + (size_t)rows * 8;
 }
 
 hipError_t launch_commit_sampled(const CommitArgs& a, float temperature, uint64_t seed, uint64_t step,
                                  hipStream_t st) {
   const int64_t rows = (int64_t)a.n_seq * a.blk_len;
   const int chunk_len = commit_chunk_len(rows, a.vocab, kSampleTargetWGs);
-  const int nchunk = (a.vocab + chunk_len - 1) / chunk_len;
+  const int nchunk = (int)(((long long)a.vocab + chunk_len - 1) / chunk_len);
   Partial* part = reinterpret_cast<Partial*>(a.ws);
   float* row_conf = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + (size_t)rows * nchunk * sizeof(Partial));
   int32_t* row_pred = reinterpret_cast<int32_t*>(row_conf + rows);
@@ -1232,8 +1234,8 @@ hipError_t launch_commit_sampled_truncated(const CommitArgs& a, float temperatur
 }
 
 int commit_chunks_per_row(long long rows, int vocab) {
-  const int len = commit_chunk_len(rows, vocab);
-  return (vocab + len - 1) / len;
+  const long long len = commit_chunk_len(rows, vocab);
+  return (int)(((long long)vocab + len - 1) / len);
 }
 
 size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab) {
@@ -1244,7 +1246,7 @@ size_t commit_workspace_bytes(int n_seq, int blk_len, int vocab) {
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.n_seq * a.blk_len;
   const int chunk_len = commit_chunk_len(rows, a.vocab);
-  const int nchunk = (a.vocab + chunk_len - 1) / chunk_len;
+  const int nchunk = (int)(((long long)a.vocab + chunk_len - 1) / chunk_len);
   Partial* part = reinterpret_cast<Partial*>(a.ws);
   const int elem = a.is_bf16 ? 2 : 4;
   const bool vec = ((uintptr_t)a.logits % 16 == 0) && ((a.row_stride * elem) % 16 == 0);

@@ -47,7 +47,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are int-sized.  In C++ their underlying type is fixed to
+ * int, so that every int a caller passes (from C, or through a binding) is a
+ * value the library may test and reject with a status. */
+#ifdef __cplusplus
+#define BD_INT_ENUM enum : int
+#else
+#define BD_INT_ENUM enum
+#endif
+
+typedef BD_INT_ENUM {
   BD_OK = 0,
   BD_ERR_NULL = 1,         /* a required pointer is NULL */
   BD_ERR_SHAPE = 2,        /* a size is non-positive or inconsistent */
@@ -60,10 +69,10 @@ typedef enum {
                               no-allocation entry point holds */
 } bd_status;
 
-typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+typedef BD_INT_ENUM { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
 
 /* What a block does when none of its masked tokens clears the threshold. */
-typedef enum {
+typedef BD_INT_ENUM {
   BD_FALLBACK_NONE = 0,  /* commit nothing; the block stays as it is */
   BD_FALLBACK_TOP1 = 1   /* commit the single most confident masked token (lowest row on ties) */
 } bd_fallback;
@@ -190,7 +199,8 @@ bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages
  *
  * logits [n_seq * blk_len rows, vocab], row r at logits + r * row_stride
  * elements (row_stride >= vocab).  Rows r = s * blk_len .. s * blk_len +
- * blk_len - 1 form the current block of sequence s.
+ * blk_len - 1 form the current block of sequence s.  vocab is at most
+ * BD_MAX_VOCAB (BD_ERR_SHAPE beyond; the workspace query then returns 0).
  *
  * For each row with masked[r] != 0 on entry:
  *   pred[r] = lowest id v with logits[r][v] = max_v logits[r][v]
@@ -212,6 +222,7 @@ bd_status bd_kv_append_block(const void* k_blk, const void* v_blk, void* k_pages
  * threshold outside (0, 1) is legal (>= 1: fallback only; < 1/vocab: every
  * masked row commits); a NaN threshold is BD_ERR_VALUE.
  * ---------------------------------------------------------------------- */
+#define BD_MAX_VOCAB (1 << 30)
 size_t bd_confidence_commit_workspace_size(int n_seq, int blk_len, int vocab);
 bd_status bd_confidence_commit(const void* logits, int64_t row_stride, int n_seq, int blk_len, int vocab,
                                bd_dtype dtype, float threshold, bd_fallback fallback,
