@@ -293,14 +293,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
     l_run += psum;
   };
 
-  // The softmax phase: its group's load of tile u into lds_tile (if any, waited
-  // for two phases later) and the softmax of tile ts (if this wave's rows see
-  // it).
-  auto s_phase = [&](uint32_t lds_tile, const uint16_t* g, int u, int ts) __attribute__((always_inline)) {
-    const bool ld = u < ntiles;
-    if (ld) load_tile(lds_tile, g, u);
+  // The softmax phase of tile ts (if this wave's rows see it).  Group B first
+  // starts its load of V(ts+2).  At the end each wave waits for its group's
+  // previous load (K(ts+1) or V(ts+1)) and leaves the one of tile ts+2 in
+  // flight.
+  auto s_phase = [&](int ts, bool load_v) __attribute__((always_inline)) {
+    const int u = ts + 2;
+    if (load_v && u < ntiles) load_tile(lds0 + kVRing + (u % kNS) * kTileBytes, vb, u);
     if (ts >= 0 && ts < ntiles && live(ts)) softmax(ts);
-    if (ld) vm_wait<4>();
+    if (u < ntiles) vm_wait<4>();
     else vm_wait<0>();
   };
 
@@ -309,9 +310,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   // products multiply P = 0 by the zero-filled V stage, and when tile t is past
   // this wave's rows (or past the last tile) the QK products run on whatever
   // the K stage holds and their result is never used.  Afterwards kaddr moves
-  // to the K stage of tile t+1 and vaddr to the V stage of tile t.
+  // to the K stage of tile t+1 and vaddr to the V stage of tile t, and group A
+  // starts its load of K(t+2).
   int kst = 0, vst = kNS - 1;   // ring stages of K(t) and V(t-1)
-  auto m_phase = [&](int t) __attribute__((always_inline)) {
+  auto m_phase = [&](int t, bool load_k) __attribute__((always_inline)) {
     if (live(t == 0 ? 0 : t - 1)) mm();
     const uint32_t dk = kst == kNS - 1 ? (uint32_t)(-(kNS - 1) * kTileBytes) : (uint32_t)kTileBytes;
     const uint32_t dv = vst == kNS - 1 ? (uint32_t)(-(kNS - 1) * kTileBytes) : (uint32_t)kTileBytes;
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
     for (int ds = 0; ds < 8; ++ds) kaddr[ds] += dk;
 #pragma unroll
     for (int y = 0; y < 8; ++y) vaddr[y] += dv;
+    if (load_k && t + 2 < ntiles) load_tile(lds0 + kKRing + ((t + 2) % kNS) * kTileBytes, kb, t + 2);
   };
 
   // Schedule.  Every tile takes two phases, each ended by a workgroup
@@ -328,25 +331,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   // S(t) = Q K(t)^T, and in phase 2t+1 the softmax of S(t); group B runs the
   // same one phase later.  So in every phase one wave of each SIMD issues
   // matrix products while the other runs its softmax on the vector ALU.
-  // Loads are issued only in softmax phases, so that the matrix phases never
-  // wait on the memory pipeline: A starts K(t+2) in phase 2t+1, B starts V(t+1)
-  // in phase 2t, and each waits for its previous load at the end of that
-  // phase, two phases after issuing it (K(t+1) is first read in phase 2t+2,
-  // V(t) in phase 2t+2).  With three stages per ring, a load never overwrites
-  // a tile still to be read: K(t-1) and V(t-2), whose stages K(t+2) and V(t+1)
-  // take, were last read in phase 2t-1.
+  // Loads: A starts K(t+2) at the end of its matrix phase 2t, where the wave
+  // only waits for its last products, so that the load issue stays off the
+  // softmax phases that bound the loop; B starts V(t+1) at the start of its
+  // softmax phase 2t.  A wave may issue its share of a tile while the other
+  // waves still work, so a load goes only into a stage no wave reads in that
+  // phase: with three stages per ring, K(t+2) and V(t+1) take the stages of
+  // K(t-1) and V(t-2), last read in phase 2t-1.  (B cannot start V(t+2) after
+  // its matrix phase 2t+1 as A does with K: its group's other waves may still
+  // read V(t-1) there, in the stage that V(t+2) would take.)  The issuing
+  // waves wait for K(t+2) at the end of phase 2t+3 and for V(t+1) at the end
+  // of phase 2t+2; both are first read in phase 2t+4.
   if (grp_a) {
     for (int t = 0; t <= ntiles; ++t) {
-      m_phase(t);
+      m_phase(t, true);
       __syncthreads();
-      s_phase(lds0 + kKRing + ((t + 2) % kNS) * kTileBytes, kb, t + 2, t);
+      s_phase(t, false);
       __syncthreads();
     }
   } else {
     for (int t = 0; t <= ntiles; ++t) {
-      s_phase(lds0 + kVRing + ((t + 1) % kNS) * kTileBytes, vb, t + 1, t - 1);
+      s_phase(t - 1, true);
       __syncthreads();
-      m_phase(t);
+      m_phase(t, false);
       __syncthreads();
     }
   }
