@@ -77,6 +77,35 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // SIMD of this wave (HW_ID bits 5:4), exchanged through LDS.  Wave groups:
+  // normally the hardware places two waves on each SIMD: group A is the first
+  // of the two (by wave index), group B the second, and gw (0..3) is the SIMD.
+  // Otherwise waves 0-3 form A and 4-7 form B, gw = wave % 4.  Either way each
+  // group has four waves with distinct gw (which split the group's tile
+  // loads); the pairing only affects speed.
+  const int simd = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* simd_of = reinterpret_cast<lds_int*>((uintptr_t)(lds0 + kIdsOff));
+  if (lane == 0) simd_of[wave] = simd;
+  __syncthreads();
+  int ids[kNW];
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) ids[w] = __builtin_amdgcn_readfirstlane(simd_of[w]);
+  bool paired = true;
+  int rank = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    int same = 0;
+#pragma unroll
+    for (int x = 0; x < kNW; ++x) same += (ids[x] == ids[w]);
+    paired = paired && same == 2;
+    rank += (w < wave && ids[w] == simd);
+  }
+  const bool grp_a = __builtin_amdgcn_readfirstlane(paired ? rank == 0 : wave < 4);
+  const int gw = __builtin_amdgcn_readfirstlane(paired ? simd : (wave & 3));
+
+  // The workgroup's work item: query tile qt (256 rows) of query head hq.
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = p.qtiles * p.G;
   const int grp = wid / per_group;
@@ -103,12 +132,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
 
-  // SIMD of this wave (HW_ID bits 5:4); exchanged through LDS below.
-  const int simd = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
-  typedef __attribute__((address_space(3))) int lds_int;
-  lds_int* simd_of = reinterpret_cast<lds_int*>((uintptr_t)(lds0 + kIdsOff));
-  if (lane == 0) simd_of[wave] = simd;
-
   // Prologue: K tiles 0 and 1 and V tile 0 (issued by all waves), and the V
   // stage of tile -1 zero-filled (the first matrix phase multiplies it by
   // P = 0).
@@ -130,27 +153,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d128(FwdParams p) {
   }
   vm_wait<0>();
   __syncthreads();
-
-  // Wave groups.  Normally the hardware places two waves on each SIMD: group A
-  // is the first of the two (by wave index), group B the second, and gw (0..3)
-  // is the SIMD.  Otherwise waves 0-3 form A and 4-7 form B, gw = wave % 4.
-  // Either way each group has four waves with distinct gw (which split the
-  // group's tile loads); the pairing only affects speed.
-  int ids[kNW];
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) ids[w] = __builtin_amdgcn_readfirstlane(simd_of[w]);
-  bool paired = true;
-  int rank = 0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    int same = 0;
-#pragma unroll
-    for (int x = 0; x < kNW; ++x) same += (ids[x] == ids[w]);
-    paired = paired && same == 2;
-    rank += (w < wave && ids[w] == simd);
-  }
-  const bool grp_a = __builtin_amdgcn_readfirstlane(paired ? rank == 0 : wave < 4);
-  const int gw = __builtin_amdgcn_readfirstlane(paired ? simd : (wave & 3));
 
   f32x16 oacc[4];
 #pragma unroll

@@ -72,6 +72,18 @@ def test_bf16_shapes(B, L, Hq, Hkv, blk):
     check_fwd(inp, "bf16", blk, o, lse)
 
 
+def test_bf16_many_query_heads():
+    # ten query heads per KV head (320 query tiles, more than one per compute
+    # unit), a ragged last tile and a block size that does not divide the
+    # 64-key tile; every row is compared, and a second call is bit-identical
+    banner("fwd bf16 B=1 L=1000 Hq=80 Hkv=8 blk=48")
+    inp = W.attention_inputs(1, 1000, 80, 8, 128, "bf16", seed=77)
+    o, lse = gpu_fwd(inp, "bf16", 48)
+    check_fwd(inp, "bf16", 48, o, lse)
+    o2, lse2 = gpu_fwd(inp, "bf16", 48)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_bf16_custom_scale():
     banner("fwd bf16 scale 0.2")
     inp = W.attention_inputs(1, 256, 2, 1, 128, "bf16", seed=3)
