@@ -31,6 +31,8 @@
 #include "bd_device.hpp"
 #include "bd_kernels.hpp"
 
+#include <algorithm>
+#include <climits>
 #include <mutex>
 #include <type_traits>
 
@@ -46,6 +48,7 @@ struct BwdParams {
   float* negD;         // [B, Hq, Lp]: -D = -rowsum(dO * O); 0 in the padding rows
   float* nlse;         // [B, Hq, Lp]: -LSE / scale; 0 in the padding rows
   uint16_t *dq, *dk, *dv;
+  unsigned* queue;     // [2][8]: next unclaimed dK/dV and dQ item of each XCD's list (zeroed by bwd_prep)
   int B, L, Lp, Hq, Hkv, G, blk;
   float scale, scale_log2;
 };
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
     p.negD[bh * p.Lp + i] = -s;
     p.nlse[bh * p.Lp + i] = -p.lse[bh * p.L + i] / p.scale;
   }
+  if (gt < 16) p.queue[gt] = 0u;
   const int pad = p.Lp - p.L;
   if (gt < (int64_t)p.B * p.Hq * pad) {
     const int64_t bh = gt / pad;
@@ -149,7 +153,8 @@ using Stage = std::integral_constant<int, S>;
 // one extra add per read).
 __device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-__global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
+// Work item wid: the 128 keys kt * 128 .. of (batch, KV head) wid / nkt.
+__device__ __forceinline__ void dkdv_item(const BwdParams& p, const int wid) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -158,7 +163,6 @@ __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) {
   const int col = lane & 31, half = lane >> 5;
   const int L = p.L;
   const int nkt = (L + kKvKeys - 1) / kKvKeys;
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = wid % nkt;
   const int bk = wid / nkt;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
@@ -436,7 +440,9 @@ constexpr int kDqNW = 8;
 constexpr int kDqStage = 2 * kTileBytes;       // K tile, V tile
 constexpr size_t kDqSmem = 2 * (size_t)kDqStage;
 
-__global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
+// Work item wid: query tile qt (256 rows) of one query head, the most
+// expensive tiles of a (batch, KV head) group first.
+__device__ __forceinline__ void dq_item(const BwdParams& p, const int wid) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -445,7 +451,6 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
   const int col = lane & 31, half = lane >> 5;
   const int L = p.L;
   const int qtiles = (L + 32 * kDqNW - 1) / (32 * kDqNW);
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = qtiles * p.G;
   const int grp = wid / per_group, rem = wid - grp * per_group;
   const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
@@ -564,11 +569,80 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) {
     }
 }
 
+static_assert(kKvNW == kDqNW, "one workgroup shape for both kinds of work item");
+
+__global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) { dkdv_item(p, xcd_remap(blockIdx.x, gridDim.x)); }
+
+__global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) { dq_item(p, xcd_remap(blockIdx.x, gridDim.x)); }
+
+// dK/dV items, then dQ items, each in a persistent launch (one workgroup
+// per compute unit), so that no compute unit idles while another XCD still
+// works: whole XCDs run at different speeds (per-CU busy time of a launch of
+// one workgroup per item differs by up to 7 % (dK/dV) and 10 % (dQ) between
+// the XCDs), and such a launch ends when its slowest XCD does.  XCD x's list
+// holds the n / 8 items xcd_remap gives it in that launch (whole (batch, KV
+// head) groups of per_group items, each group's most expensive first), the
+// groups interleaved (first item of each, then second, ...), so the list
+// runs from the XCD's most to its least expensive items and its last round
+// is short.  A workgroup claims the next
+// item of its own XCD's list (XCC_ID) with an atomic counter and, once that
+// list is used up, of the other XCDs' lists in turn; every workgroup stops
+// when all lists are, so the loop always ends.  The counters only hand out
+// items: each output is computed by one workgroup in one fixed order
+// whichever claims it, so the results do not depend on the schedule.  (One
+// launch for both kinds of item measured 0.6 % slower than two: the two
+// bodies in one loop spill scalar registers inside the dQ products.)
+template <bool kDq>
+__global__ __launch_bounds__(kKvNW * 64) void bwd_queued(BwdParams p, int n, int per_group) {
+  constexpr int kXcd = 8;
+  __shared__ int pick[2];
+  unsigned* queue = p.queue + (kDq ? kXcd : 0);
+  const int per = n / kXcd;
+  const int groups = per % per_group == 0 ? per / per_group : 1;   // whole groups per XCD
+  const int stride = groups > 1 ? per_group : 0;
+  int from = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcd - 1));   // XCC_ID
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int q = -1, it = 0;
+      for (int y = 0; y < kXcd && q < 0; ++y) {
+        const int qq = (from + y) & (kXcd - 1);
+        const int i = (int)atomicAdd(queue + qq, 1u);
+        if (i < per) {
+          q = qq;
+          it = i;
+        }
+      }
+      pick[0] = q;
+      pick[1] = it;
+    }
+    __syncthreads();
+    const int q = pick[0], it = pick[1];
+    __syncthreads();   // pick is rewritten only after every wave has read it
+    if (q < 0) break;
+    from = q;
+    const int w = q * per + (it % groups) * stride + it / groups;
+    if (kDq) dq_item(p, w);
+    else dkdv_item(p, w);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = -1;
+  return cus[dev];
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int batch, int seqlen, int n_q_heads) {
   const size_t lp = ((size_t)seqlen + 63) / 64 * 64;
-  return 2 * (size_t)batch * n_q_heads * lp * sizeof(float) + 16;
+  return 2 * (size_t)batch * n_q_heads * lp * sizeof(float) + 64;   // -D, -LSE/scale, 16 work counters
 }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -582,6 +656,12 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
     if (attr_err == hipSuccess)
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDqSmem);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_queued<false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkdvSmem);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_queued<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDqSmem);
   });
   if (attr_err != hipSuccess) return attr_err;
   BwdParams p;
@@ -594,6 +674,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.Lp = (s.seqlen + 63) / 64 * 64;
   p.negD = static_cast<float*>(ws);
   p.nlse = p.negD + (size_t)s.batch * s.n_q_heads * p.Lp;
+  p.queue = reinterpret_cast<unsigned*>(p.nlse + (size_t)s.batch * s.n_q_heads * p.Lp);
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
@@ -612,10 +693,22 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + kKvKeys - 1) / kKvKeys);
+  const long long nq = (long long)s.batch * s.n_q_heads * ((s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW));
+  const int cus = device_cus();
+  if (nk % 8 == 0 && nq % 8 == 0 && cus > 0 && nk <= INT_MAX && nq <= INT_MAX) {
+    const int nkt = (s.seqlen + kKvKeys - 1) / kKvKeys;
+    const int nqt = (s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW);
+    hipLaunchKernelGGL(bwd_queued<false>, dim3((unsigned)std::min<long long>(cus, nk)), dim3(kKvNW * 64), kDkdvSmem,
+                       st, p, (int)nk, nkt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_queued<true>, dim3((unsigned)std::min<long long>(cus, nq)), dim3(kDqNW * 64), kDqSmem,
+                       st, p, (int)nq, nqt * (s.n_q_heads / s.n_kv_heads));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)nk), dim3(kKvNW * 64), kDkdvSmem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nq = (long long)s.batch * s.n_q_heads * ((s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW));
   hipLaunchKernelGGL(bwd_dq, dim3((unsigned)nq), dim3(kDqNW * 64), kDqSmem, st, p);
   return hipGetLastError();
 }

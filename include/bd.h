@@ -108,10 +108,14 @@ bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   dk, dv [batch, seqlen, n_kv_heads, head_dim]   out (summed over the query
  *        heads of each group)
  *   workspace of bd_attn_bwd_workspace_size() bytes (holds, per row, D =
- *        rowsum(d_o * o) and lse * log2(e) in float32); contents on entry are
+ *        rowsum(d_o * o) and lse * log2(e) in float32, and the counters that
+ *        hand out work items to the compute units); contents on entry are
  *        ignored.
  *
- * Supported: as bd_attn_fwd.  Deterministic: no atomics.
+ * Supported: as bd_attn_fwd.  Deterministic: every output element is summed
+ * by one workgroup in one fixed order (the counters only decide which
+ * workgroup computes which block of outputs), so repeated calls give
+ * bit-identical results.
  * ---------------------------------------------------------------------- */
 size_t bd_attn_bwd_workspace_size(int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim);
 bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -67,6 +67,13 @@ hipError_t hipGetDevice(int* device) {
   return hipSuccess;
 }
 
+// The compute units of an MI355X; other attributes are not asked for.
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
+  if (!value || device != 0 || attr != hipDeviceAttributeMultiprocessorCount) return hipErrorInvalidValue;
+  *value = 256;
+  return hipSuccess;
+}
+
 hipError_t hipGetLastError(void) { return hipSuccess; }
 
 // A host stand-in address (no launch is run, so it is never dereferenced).

@@ -57,7 +57,7 @@ def test_fwd_validation():
 
 def test_bwd_validation():
     ws = L.lib.bd_attn_bwd_workspace_size(1, 64, 2, 1, 128)
-    assert ws == 1 * 2 * 64 * 8 + 16
+    assert ws == 1 * 2 * 64 * 8 + 64        # -D and -LSE/scale per row, then the work counters
     args = [FAKE] * 9 + [FAKE, ws, 1, 64, 2, 1, 128, 32, 0.0, L.BD_BF16, None]
     bad = list(args); bad[4] = None
     assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_NULL          # lse is required

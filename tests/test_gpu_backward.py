@@ -58,6 +58,9 @@ def check(inp, dtype, blk, grads, q_block_start=0, batches=None, scale=None):
     (1, 333, 4, 1, 48),
     (1, 1, 1, 1, 32),
     (1, 130, 2, 2, 7),
+    # dK/dV and dQ items counts divisible by 8: both run in one launch
+    (2, 1000, 8, 2, 32),     # 32 dK/dV and 64 dQ items, ragged last tiles
+    (1, 512, 16, 8, 48),     # 32 of each, block not dividing the tiles
 ])
 def test_bf16_shapes(B, L, Hq, Hkv, blk):
     banner(f"bwd bf16 B={B} L={L} Hq={Hq} Hkv={Hkv} blk={blk}")
@@ -65,9 +68,10 @@ def test_bf16_shapes(B, L, Hq, Hkv, blk):
     check(inp, "bf16", blk, gpu_fwd_bwd(inp, "bf16", blk))
 
 
-def test_bf16_scale_and_determinism():
-    banner("bwd bf16 custom scale, determinism")
-    inp = W.attention_inputs(1, 384, 4, 2, 128, "bf16", seed=5, with_grad=True)
+@pytest.mark.parametrize("L", [384, 512])   # 512: dK/dV and dQ in one launch
+def test_bf16_scale_and_determinism(L):
+    banner(f"bwd bf16 custom scale, determinism, L={L}")
+    inp = W.attention_inputs(1, L, 4, 2, 128, "bf16", seed=5, with_grad=True)
     g1 = gpu_fwd_bwd(inp, "bf16", 32, scale=0.3)
     check(inp, "bf16", 32, g1, scale=0.3)
     g2 = gpu_fwd_bwd(inp, "bf16", 32, scale=0.3)
