@@ -584,14 +584,14 @@ __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) { dq_item(p, x
 // head) groups of per_group items, each group's most expensive first), the
 // groups interleaved (first item of each, then second, ...), so the list
 // runs from the XCD's most to its least expensive items and its last round
-// is short.  A workgroup claims the next
-// item of its own XCD's list (XCC_ID) with an atomic counter and, once that
-// list is used up, of the other XCDs' lists in turn; every workgroup stops
-// when all lists are, so the loop always ends.  The counters only hand out
-// items: each output is computed by one workgroup in one fixed order
-// whichever claims it, so the results do not depend on the schedule.  (One
-// launch for both kinds of item measured 0.6 % slower than two: the two
-// bodies in one loop spill scalar registers inside the dQ products.)
+// is short.  A workgroup claims the next item of its own XCD's list
+// (XCC_ID) with an atomic counter and, once that list is used up, of the
+// other XCDs' lists in turn; every workgroup stops when all lists are, so the
+// loop always ends.  The counters only hand out items: each output is
+// computed by one workgroup in one fixed order whichever claims it, so the
+// results do not depend on the schedule.  (The two kinds of item get a launch
+// each: with both bodies in one loop the compiler spills scalar registers
+// inside the dQ products.)
 template <bool kDq>
 __global__ __launch_bounds__(kKvNW * 64) void bwd_queued(BwdParams p, int n, int per_group) {
   constexpr int kXcd = 8;
