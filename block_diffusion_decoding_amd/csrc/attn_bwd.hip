@@ -48,7 +48,7 @@ struct BwdParams {
   float* negD;         // [B, Hq, Lp]: -D = -rowsum(dO * O); 0 in the padding rows
   float* nlse;         // [B, Hq, Lp]: -LSE / scale; 0 in the padding rows
   uint16_t *dq, *dk, *dv;
-  unsigned* queue;     // [2][8]: next unclaimed dK/dV and dQ item of each XCD's list (zeroed by bwd_prep)
+  unsigned* queue;     // [8]: next unclaimed item of each XCD's list (zeroed by bwd_prep)
   int B, L, Lp, Hq, Hkv, G, blk;
   float scale, scale_log2;
 };
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
     p.negD[bh * p.Lp + i] = -s;
     p.nlse[bh * p.Lp + i] = -p.lse[bh * p.L + i] / p.scale;
   }
-  if (gt < 16) p.queue[gt] = 0u;
+  if (gt < 8) p.queue[gt] = 0u;
   const int pad = p.Lp - p.L;
   if (gt < (int64_t)p.B * p.Hq * pad) {
     const int64_t bh = gt / pad;
@@ -570,43 +570,41 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, const int wid) {
 }
 
 static_assert(kKvNW == kDqNW, "one workgroup shape for both kinds of work item");
+constexpr size_t kQueuedSmem = kDkdvSmem > kDqSmem ? kDkdvSmem : kDqSmem;
 
 __global__ __launch_bounds__(kKvNW * 64) void bwd_dkdv(BwdParams p) { dkdv_item(p, xcd_remap(blockIdx.x, gridDim.x)); }
 
 __global__ __launch_bounds__(kDqNW * 64) void bwd_dq(BwdParams p) { dq_item(p, xcd_remap(blockIdx.x, gridDim.x)); }
 
-// dK/dV items, then dQ items, each in a persistent launch (one workgroup
-// per compute unit), so that no compute unit idles while another XCD still
-// works: whole XCDs run at different speeds (per-CU busy time of a launch of
-// one workgroup per item differs by up to 7 % (dK/dV) and 10 % (dQ) between
-// the XCDs), and such a launch ends when its slowest XCD does.  XCD x's list
-// holds the n / 8 items xcd_remap gives it in that launch (whole (batch, KV
-// head) groups of per_group items, each group's most expensive first), the
-// groups interleaved (first item of each, then second, ...), so the list
-// runs from the XCD's most to its least expensive items and its last round
-// is short.  A workgroup claims the next item of its own XCD's list
-// (XCC_ID) with an atomic counter and, once that list is used up, of the
-// other XCDs' lists in turn; every workgroup stops when all lists are, so the
-// loop always ends.  The counters only hand out items: each output is
-// computed by one workgroup in one fixed order whichever claims it, so the
-// results do not depend on the schedule.  (The two kinds of item get a launch
-// each: with both bodies in one loop the compiler spills scalar registers
-// inside the dQ products.)
-template <bool kDq>
-__global__ __launch_bounds__(kKvNW * 64) void bwd_queued(BwdParams p, int n, int per_group) {
+// dK/dV and dQ items in one persistent launch (one workgroup per compute
+// unit), so that no compute unit idles while another XCD still works: whole
+// XCDs run at different clocks (per-CU busy time of a launch of one
+// workgroup per item differs by up to 7 % (dK/dV) and 10 % (dQ) between the
+// XCDs), and such a launch ends when its slowest XCD does.  XCD x's list
+// holds the items xcd_remap gives it in the per-item launches: its nk / 8
+// dK/dV items, then its nq / 8 dQ items, each kind's whole (batch, KV head)
+// groups interleaved (first item of each group, then the second, ...; within
+// a group the most expensive first), so each kind runs from its most to its
+// least expensive items and the list ends on small dQ items.  A workgroup
+// claims the next item of its own XCD's list (XCC_ID) with an atomic counter
+// and, once that list is used up, of the other XCDs' lists in turn; every
+// workgroup stops when all lists are, so the loop always ends.  The counters
+// only hand out items: each output is computed by one workgroup in one fixed
+// order whichever claims it, so the results do not depend on the schedule.
+__global__ __launch_bounds__(kKvNW * 64) void bwd_queued(BwdParams p, int nk, int nq, int pgk, int pgq) {
   constexpr int kXcd = 8;
   __shared__ int pick[2];
-  unsigned* queue = p.queue + (kDq ? kXcd : 0);
-  const int per = n / kXcd;
-  const int groups = per % per_group == 0 ? per / per_group : 1;   // whole groups per XCD
-  const int stride = groups > 1 ? per_group : 0;
+  const int a = nk / kXcd, bq = nq / kXcd, per = a + bq;
+  // groups per XCD and their stride (1 and 0 when a group spans XCDs)
+  const int gk = a % pgk == 0 ? a / pgk : 1, sk = gk > 1 ? pgk : 0;
+  const int gq = bq % pgq == 0 ? bq / pgq : 1, sq = gq > 1 ? pgq : 0;
   int from = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcd - 1));   // XCC_ID
   for (;;) {
     if (threadIdx.x == 0) {
       int q = -1, it = 0;
       for (int y = 0; y < kXcd && q < 0; ++y) {
         const int qq = (from + y) & (kXcd - 1);
-        const int i = (int)atomicAdd(queue + qq, 1u);
+        const int i = (int)atomicAdd(p.queue + qq, 1u);
         if (i < per) {
           q = qq;
           it = i;
@@ -620,9 +618,12 @@ __global__ __launch_bounds__(kKvNW * 64) void bwd_queued(BwdParams p, int n, int
     __syncthreads();   // pick is rewritten only after every wave has read it
     if (q < 0) break;
     from = q;
-    const int w = q * per + (it % groups) * stride + it / groups;
-    if (kDq) dq_item(p, w);
-    else dkdv_item(p, w);
+    if (it < a) {
+      dkdv_item(p, q * a + (it % gk) * sk + it / gk);
+    } else {
+      const int j = it - a;
+      dq_item(p, q * bq + (j % gq) * sq + j / gq);
+    }
   }
 }
 
@@ -642,7 +643,7 @@ int device_cus() {
 
 size_t attn_bwd_workspace_bytes(int batch, int seqlen, int n_q_heads) {
   const size_t lp = ((size_t)seqlen + 63) / 64 * 64;
-  return 2 * (size_t)batch * n_q_heads * lp * sizeof(float) + 64;   // -D, -LSE/scale, 16 work counters
+  return 2 * (size_t)batch * n_q_heads * lp * sizeof(float) + 64;   // -D, -LSE/scale, 8 work counters
 }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -657,11 +658,8 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
       attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDqSmem);
     if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_queued<false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkdvSmem);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_queued<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDqSmem);
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_queued),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQueuedSmem);
   });
   if (attr_err != hipSuccess) return attr_err;
   BwdParams p;
@@ -695,15 +693,11 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   const long long nk = (long long)s.batch * s.n_kv_heads * ((s.seqlen + kKvKeys - 1) / kKvKeys);
   const long long nq = (long long)s.batch * s.n_q_heads * ((s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW));
   const int cus = device_cus();
-  if (nk % 8 == 0 && nq % 8 == 0 && cus > 0 && nk <= INT_MAX && nq <= INT_MAX) {
+  if (nk % 8 == 0 && nq % 8 == 0 && cus > 0 && nk + nq <= INT_MAX) {
     const int nkt = (s.seqlen + kKvKeys - 1) / kKvKeys;
     const int nqt = (s.seqlen + 32 * kDqNW - 1) / (32 * kDqNW);
-    hipLaunchKernelGGL(bwd_queued<false>, dim3((unsigned)std::min<long long>(cus, nk)), dim3(kKvNW * 64), kDkdvSmem,
-                       st, p, (int)nk, nkt);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_queued<true>, dim3((unsigned)std::min<long long>(cus, nq)), dim3(kDqNW * 64), kDqSmem,
-                       st, p, (int)nq, nqt * (s.n_q_heads / s.n_kv_heads));
+    hipLaunchKernelGGL(bwd_queued, dim3((unsigned)std::min<long long>(cus, nk + nq)), dim3(kKvNW * 64), kQueuedSmem,
+                       st, p, (int)nk, (int)nq, nkt, nqt * (s.n_q_heads / s.n_kv_heads));
     return hipGetLastError();
   }
   hipLaunchKernelGGL(bwd_dkdv, dim3((unsigned)nk), dim3(kKvNW * 64), kDkdvSmem, st, p);
