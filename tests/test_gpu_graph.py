@@ -1,5 +1,5 @@
 """Graph capture of the hot path: a forward, a decode step and the commit (greedy and sampled),
-captured with every buffer allocated beforehand, replayed several times with eager work and
+and the backward, captured with every buffer allocated beforehand, replayed several times with eager work and
 synchronisations between the replays; every replay must reproduce the eager results bit for bit
 (the kernels are deterministic and the library issues no memory fills or allocations)."""
 import numpy as np
@@ -101,3 +101,39 @@ def test_graph_replays_equal_eager():
         bd.bd_confidence_commit(lg, tok0.clone(), msk0.clone(), 32, 0.9, workspace=cws)
         torch.cuda.synchronize()
     print("  4 replays bit-identical to the eager step")
+
+
+def test_graph_backward_replays_equal_eager():
+    # 1 x 512 tokens, 16 / 8 heads: 32 dK/dV and 32 dQ items, so the backward runs as
+    # one persistent launch whose work counters (in the workspace) the prep kernel
+    # zeroes; the workspace is filled with 0xFF before every replay.
+    banner("graph capture: backward (queued launch)")
+    torch.cuda.synchronize()
+    a = W.attention_inputs(1, 512, 16, 8, 128, "bf16", seed=21, with_grad=True)
+    q, k, v, d_o = (dev(a[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = bd.bd_attn_fwd(q, k, v, 32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(bd.bd_attn_bwd_workspace_size(1, 512, 16, 8, 128), dtype=torch.uint8, device="cuda")
+
+    def step():
+        bd.bd_attn_bwd(q, k, v, o, lse, d_o, 32, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (dq, dk, dv)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        ws.fill_(0xFF)
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(eager, (dq, dk, dv))):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}: gradient {i} differs"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+    print("  4 replays bit-identical to the eager backward")
