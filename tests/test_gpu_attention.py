@@ -64,6 +64,7 @@ def test_f32_shapes(B, L, Hq, Hkv, d, blk):
     (1, 333, 4, 1, 48),      # block not dividing the 64-key tile
     (1, 1, 1, 1, 32),        # single token
     (1, 130, 2, 2, 7),
+    (1, 300, 16, 1, 32),     # sixteen query heads per KV head (multi-query)
 ])
 def test_bf16_shapes(B, L, Hq, Hkv, blk):
     banner(f"fwd bf16 B={B} L={L} Hq={Hq} Hkv={Hkv} blk={blk}")
@@ -172,6 +173,7 @@ def test_decode_step_workload():
     ([70, 2], 40, 8, 2),         # rows = 160: three row tiles
     ([4096 + 5], 32, 16, 8),
     (list(range(0, 1500, 10)), 32, 16, 8),   # 150 sequences: the line scan spans several wave chunks
+    ([100, 2000, 0], 32, 16, 1),  # sixteen query heads per KV head: 512 rows, eight row tiles
 ])
 def test_decode_ragged(plens, T, Hq, Hkv):
     banner(f"decode bf16 plens={plens} T={T} Hq={Hq} Hkv={Hkv}")

@@ -62,6 +62,7 @@ def check(inp, dtype, blk, grads, q_block_start=0, batches=None, scale=None):
     (2, 1000, 8, 2, 32),     # 32 dK/dV and 64 dQ items, ragged last tiles
     (1, 512, 16, 8, 48),     # 32 of each, block not dividing the tiles
     (2, 512, 16, 8, 32),     # two (batch, KV head) groups per XCD list, interleaved
+    (1, 300, 16, 1, 32),     # sixteen query heads per KV head (multi-query)
 ])
 def test_bf16_shapes(B, L, Hq, Hkv, blk):
     banner(f"bwd bf16 B={B} L={L} Hq={Hq} Hkv={Hkv} blk={blk}")
