@@ -84,6 +84,8 @@ bd_status commit_common(const void* logits, int64_t row_stride, int n_seq, int b
     if (need > bd::kNoAllocScratchBytes) return BD_ERR_SCRATCH;
   } else if (!workspace || ws_bytes < need) {
     return BD_ERR_WORKSPACE;
+  } else if (!aligned16(workspace)) {
+    return BD_ERR_ALIGNMENT;
   }
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, thresholds,
                    fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
@@ -105,7 +107,7 @@ const char* bd_status_string(bd_status s) {
     case BD_ERR_WORKSPACE: return "workspace missing or too small";
     case BD_ERR_VALUE: return "scalar argument out of its domain";
     case BD_ERR_HIP: return "HIP runtime error";
-    case BD_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case BD_ERR_ALIGNMENT: return "tensor or workspace pointer not 16-byte aligned";
     case BD_ERR_SCRATCH: return "problem exceeds the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
@@ -146,6 +148,7 @@ bd_status bd_attn_bwd(const void* q, const void* k, const void* v, const void* o
   if (st != BD_OK) return st;
   const size_t need = bd::attn_bwd_workspace_bytes(batch, seqlen, n_q_heads);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BD_ERR_ALIGNMENT;
   bd::AttnShape s{batch, seqlen, n_q_heads, n_kv_heads, head_dim, block_size,
                   resolve_scale(softmax_scale, head_dim)};
   if (dtype == BD_BF16) {
@@ -190,6 +193,7 @@ bd_status bd_attn_decode_block(const void* q_blk, const void* k_blk, const void*
       return BD_ERR_ALIGNMENT;
     const size_t need = bd::decode_workspace_bytes(s, 1);
     if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return BD_ERR_ALIGNMENT;
     return hip_status(bd::launch_decode_bf16(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_start, prefix_len, o,
                                              lse, workspace, s, stream));
   }
@@ -221,6 +225,7 @@ bd_status bd_attn_decode_block_paged(const void* q_blk, const void* k_blk, const
                     resolve_scale(softmax_scale, head_dim)};
   const size_t need = bd::decode_workspace_bytes(s, 1);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BD_ERR_ALIGNMENT;
   return hip_status(bd::launch_decode_bf16_paged(q_blk, k_blk, v_blk, k_pages, v_pages, block_table,
                                                  max_pages_per_seq, page_size, prefix_len, o, lse, workspace, s,
                                                  stream));
@@ -299,6 +304,7 @@ bd_status bd_confidence_commit_sampled(const void* logits, int64_t row_stride, i
   if (!commit_rows_ok(n_seq, blk_len, vocab)) return BD_ERR_SHAPE;
   const size_t need = bd::commit_sampled_workspace_bytes(n_seq, blk_len, vocab);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BD_ERR_ALIGNMENT;
   bd::CommitArgs a{logits, row_stride, n_seq, blk_len, vocab, dtype == BD_BF16, threshold, nullptr,
                    fallback == BD_FALLBACK_TOP1, tokens, masked, conf, pred, n_committed, n_masked_left, workspace};
   if (truncate)
@@ -328,6 +334,7 @@ bd_status bd_lmhead_commit(const void* hidden, int64_t hidden_stride, const void
   if ((long long)n_seq * blk_len > kMaxGrid / 256) return BD_ERR_SHAPE;
   const size_t need = bd::lmhead_workspace_bytes(n_seq, blk_len);
   if (!workspace || ws_bytes < need) return BD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BD_ERR_ALIGNMENT;
   bd::LmHeadArgs a;
   a.hidden = hidden;
   a.hidden_stride = hidden_stride;

@@ -14,7 +14,9 @@
  * Conventions shared by every entry point:
  *   - Every buffer argument is DEVICE memory owned by the caller.  The library
  *     never allocates or frees memory; scratch space is the caller's
- *     `workspace`, sized by the matching *_workspace_size() query.
+ *     `workspace`, sized by the matching *_workspace_size() query, whose base
+ *     must be 16-byte aligned (BD_ERR_ALIGNMENT otherwise; hipMalloc returns
+ *     such addresses).
  *   - Tensors are dense and row-major with the innermost dimension last:
  *     q/o [batch, seqlen, n_q_heads, head_dim], k/v [batch, seqlen, n_kv_heads,
  *     head_dim] ("BSHD"); lse [batch, n_q_heads, seqlen] float32, natural log.
@@ -64,7 +66,7 @@ typedef BD_INT_ENUM {
   BD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the query returns */
   BD_ERR_VALUE = 5,        /* a scalar argument is out of its domain (e.g. NaN threshold) */
   BD_ERR_HIP = 6,          /* a HIP runtime call failed */
-  BD_ERR_ALIGNMENT = 7,    /* a bf16 tensor pointer is not 16-byte aligned */
+  BD_ERR_ALIGNMENT = 7,    /* a bf16 tensor or workspace pointer is not 16-byte aligned */
   BD_ERR_SCRATCH = 8       /* the problem needs more scratch than the fixed buffer of a
                               no-allocation entry point holds */
 } bd_status;

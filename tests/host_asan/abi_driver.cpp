@@ -91,6 +91,9 @@ void attention_backward() {
          BD_ERR_WORKSPACE);
   EXPECT(bd_attn_bwd(P, P, P, P, F, P, P, M, P, P, ws, 2, 16384, 16, 8, 128, 32, 0.f, BD_BF16, S0),
          BD_ERR_ALIGNMENT);
+  EXPECT(bd_attn_bwd(P, P, P, P, F, P, P, P, P, M, ws, 2, 16384, 16, 8, 128, 32, 0.f, BD_BF16, S0),
+         BD_ERR_ALIGNMENT);
+  EXPECT(bd_attn_bwd(P, P, P, P, F, P, P, P, P, M, kHuge, 2, 100, 4, 4, 32, 16, 0.f, BD_F32, S0), BD_ERR_ALIGNMENT);
   EXPECT(bd_attn_bwd(P, P, P, P, F, P, P, P, P, P, kHuge, INT_MAX, INT_MAX, INT_MAX, 1, 128, 32, 0.f, BD_BF16,
                      S0),
          BD_ERR_SHAPE);
@@ -127,6 +130,8 @@ void decode() {
   EXPECT(bd_attn_decode_block(P, P, P, P, P, I64, I32, 16384, P, F, 64, 32, 16, 8, 128, 0.f, BD_BF16, P, ws - 1,
                               S0),
          BD_ERR_WORKSPACE);
+  EXPECT(bd_attn_decode_block(P, P, P, P, P, I64, I32, 16384, P, F, 64, 32, 16, 8, 128, 0.f, BD_BF16, M, ws, S0),
+         BD_ERR_ALIGNMENT);
   EXPECT(bd_attn_decode_block(P, P, P, P, P, I64, I32, 16384, P, F, 64, 32, 16, 8, 128, kNaN, BD_BF16, P, ws, S0),
          BD_ERR_VALUE);
   EXPECT(bd_attn_decode_block(P, P, P, P, P, I64, I32, 16384, P, F, 64, 32, 16, 8, 128, 0.f, BD_BF16, P, ws, S0),
@@ -172,6 +177,9 @@ void decode_paged() {
   EXPECT(bd_attn_decode_block_paged(P, P, P, P, P, I32, 8, 32, I32, 200, P, F, 2, 32, 16, 8, 128, 0.f, BD_BF16, P,
                                     0, S0),
          BD_ERR_WORKSPACE);
+  EXPECT(bd_attn_decode_block_paged(P, P, P, P, P, I32, 8, 32, I32, 200, P, F, 2, 32, 16, 8, 128, 0.f, BD_BF16, M,
+                                    kHuge, S0),
+         BD_ERR_ALIGNMENT);
   EXPECT(bd_attn_decode_block_paged(P, P, P, P, P, I32, 8, 32, I32, 200, P, F, 2, 32, 16, 8, 128, 0.f, BD_BF16, P,
                                     kHuge, S0),
          BD_OK);
@@ -221,6 +229,12 @@ void commit() {
   EXPECT(bd_confidence_commit(P, V, 64, 32, V, BD_BF16, 0.95f, BD_FALLBACK_TOP1, I32, U8, F, I32, I32, I32, P,
                               ws - 1, S0),
          BD_ERR_WORKSPACE);
+  EXPECT(bd_confidence_commit(P, V, 64, 32, V, BD_BF16, 0.95f, BD_FALLBACK_TOP1, I32, U8, F, I32, I32, I32, M,
+                              ws, S0),
+         BD_ERR_ALIGNMENT);
+  EXPECT(bd_confidence_commit_rowwise(P, V, 64, 32, V, BD_BF16, F, BD_FALLBACK_TOP1, I32, U8, F, I32, I32, I32, M,
+                                      ws, S0),
+         BD_ERR_ALIGNMENT);
   EXPECT(bd_confidence_commit(P, INT64_MAX, INT_MAX, 1024, INT_MAX, BD_BF16, 0.95f, BD_FALLBACK_TOP1, I32, U8, F,
                               I32, I32, I32, P, kHuge, S0),
          BD_ERR_SHAPE);
@@ -273,6 +287,9 @@ void commit_sampled() {
   EXPECT(call(64, V, 1.f, 0, 1.f, kNaN, ws), BD_ERR_VALUE);
   EXPECT(call(64, 155649, 1.f, 50, 1.f, 0.9f, kHuge), BD_ERR_UNSUPPORTED);
   EXPECT(call(64, V, 1.f, 0, 1.f, 0.9f, ws - 1), BD_ERR_WORKSPACE);
+  EXPECT(bd_confidence_commit_sampled(P, V, 64, 32, V, BD_BF16, 1.f, 7, 3, 0, 1.f, 0.9f, BD_FALLBACK_TOP1, I32, U8,
+                                      F, I32, I32, I32, M, ws, S0),
+         BD_ERR_ALIGNMENT);
   EXPECT(call(INT_MAX / 32, INT_MAX, 1.f, 0, 1.f, 0.9f, kHuge), BD_ERR_SHAPE);
   EXPECT(call(64, V, 1.f, 0, 1.f, 0.9f, ws), BD_OK);
   EXPECT(call(64, V, 0.7f, 50, 1.f, 0.9f, ws), BD_OK);
@@ -299,6 +316,8 @@ void lmhead() {
   EXPECT(call(P, H, H, 1, H, kNaN, ws), BD_ERR_VALUE);
   EXPECT(call(P, H, H, INT_MAX, H, 0.9f, kHuge), BD_ERR_SHAPE);
   EXPECT(call(P, H, H, 1, H, 0.9f, ws - 1), BD_ERR_WORKSPACE);
+  EXPECT(bd_lmhead_commit(P, H, P, H, 1, 32, H, V, 0.9f, BD_FALLBACK_TOP1, I32, U8, F, I32, I32, I32, M, ws, S0),
+         BD_ERR_ALIGNMENT);
   EXPECT(call(P, H, H, 1, H, 0.9f, ws), BD_OK);
   EXPECT(call(P, 1024, 1024, 4, 1024, 0.5f, kHuge), BD_OK);
 }

@@ -69,6 +69,8 @@ def test_bwd_validation():
     assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_SHAPE
     bad = list(args); bad[5] = MIS
     assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_ALIGNMENT
+    bad = list(args); bad[9] = MIS
+    assert L.lib.bd_attn_bwd(*bad) == L.BD_ERR_ALIGNMENT     # the workspace too
 
 
 def test_decode_validation():
@@ -93,6 +95,7 @@ def test_decode_validation():
     assert call(ws=None) == L.BD_ERR_WORKSPACE
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
     assert call(kc=MIS) == L.BD_ERR_ALIGNMENT
+    assert call(ws=MIS) == L.BD_ERR_ALIGNMENT
     assert call(sc=math.nan) == L.BD_ERR_VALUE
 
 
@@ -117,6 +120,7 @@ def test_commit_validation():
     assert call(fb=7) == L.BD_ERR_VALUE
     assert call(ws=None) == L.BD_ERR_WORKSPACE
     assert call(nb=ws - 16) == L.BD_ERR_WORKSPACE
+    assert call(ws=MIS) == L.BD_ERR_ALIGNMENT
 
     def call_rw(**kw):
         a = dict(lg=FAKE, stride=151936, n=2, T=32, V=151936, dt=L.BD_BF16, thr=FAKE, fb=1, tok=FAKE, msk=FAKE,
@@ -131,6 +135,7 @@ def test_commit_validation():
     assert call_rw(T=2048) == L.BD_ERR_UNSUPPORTED
     assert call_rw(fb=7) == L.BD_ERR_VALUE
     assert call_rw(nb=ws - 16) == L.BD_ERR_WORKSPACE
+    assert call_rw(ws=MIS) == L.BD_ERR_ALIGNMENT
 
 
 def test_sampled_commit_validation():
@@ -152,6 +157,7 @@ def test_sampled_commit_validation():
     assert call(tau=math.nan) == L.BD_ERR_VALUE
     assert call(thr=math.nan) == L.BD_ERR_VALUE
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+    assert call(ws=MIS) == L.BD_ERR_ALIGNMENT
     assert call(seed=2**64 - 1, step=2**63, nb=0) == L.BD_ERR_WORKSPACE    # 64-bit arguments pass through
     # truncation: top_k >= 0, 0 < top_p <= 1; rows held in registers bound the vocabulary
     assert call(k=-1) == L.BD_ERR_VALUE
@@ -185,6 +191,7 @@ def test_paged_validation():
     assert call(dt=L.BD_F32) == L.BD_ERR_UNSUPPORTED
     assert call(kp=MIS) == L.BD_ERR_ALIGNMENT
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+    assert call(ws=MIS) == L.BD_ERR_ALIGNMENT
 
     def app(**kw):
         a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, mp=64, ps=64, pl=FAKE, nml=None, n=1, T=32, hkv=8, d=128,
@@ -222,6 +229,7 @@ def test_lmhead_validation():
     assert call(thr=math.nan) == L.BD_ERR_VALUE
     assert call(fb=3) == L.BD_ERR_VALUE
     assert call(nb=ws - 1) == L.BD_ERR_WORKSPACE
+    assert call(ws=MIS) == L.BD_ERR_ALIGNMENT
 
 
 def test_binding_refuses_host_tensors():
