@@ -43,9 +43,11 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
-    if not t.is_cuda:
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -54,11 +56,33 @@ def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _out(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> Optional[torch.Tensor]:
+    """A caller-supplied output (or None): the kernels write exactly `shape` elements of `dtype` to it."""
+    if t is not None:
+        _need(t, name, shape, dtype, device)
+    return t
+
+
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
     if given is not None:
+        _need(given, "workspace", device=device)
         return given, given.numel() * given.element_size()
     n = max(int(nbytes), 16)
     return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def _row_outputs(rows: int, n_seq: int, dev, want_rows: bool, conf, pred, n_committed, n_masked_left):
+    """The commit's optional outputs: caller-supplied ones checked, missing ones allocated."""
+    conf = _out(conf, "conf", (rows,), torch.float32, dev)
+    pred = _out(pred, "pred", (rows,), torch.int32, dev)
+    n_committed = _out(n_committed, "n_committed", (n_seq,), torch.int32, dev)
+    n_masked_left = _out(n_masked_left, "n_masked_left", (n_seq,), torch.int32, dev)
+    if want_rows:
+        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
+        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
+    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
+    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    return conf, pred, n_committed, n_masked_left
 
 
 # ---------------------------------------------------------------------------
@@ -68,15 +92,15 @@ def bd_attn_fwd(q, k, v, block_size: int = 32, softmax_scale: float = 0.0, o=Non
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q")
-    _need(k, "k", (B, L, Hkv, d), q.dtype)
-    _need(v, "v", (B, L, Hkv, d), q.dtype)
+    _need(k, "k", (B, L, Hkv, d), q.dtype, q.device)
+    _need(v, "v", (B, L, Hkv, d), q.dtype, q.device)
     if o is None:
         o = torch.empty_like(q)
-    _need(o, "o", q.shape, q.dtype)
+    _need(o, "o", q.shape, q.dtype, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _need(lse, "lse", (B, Hq, L), torch.float32)
+        _need(lse, "lse", (B, Hq, L), torch.float32, q.device)
     st = lib.bd_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, L, Hq, Hkv, d, block_size,
                          float(softmax_scale), _dtype_code(q), _stream(stream))
     check(st, "bd_attn_fwd")
@@ -94,11 +118,11 @@ def bd_attn_bwd(q, k, v, o, lse, d_o, block_size: int = 32, softmax_scale: float
     Hkv = k.shape[2]
     for t, n, shp in ((q, "q", None), (k, "k", (B, L, Hkv, d)), (v, "v", (B, L, Hkv, d)), (o, "o", q.shape),
                       (d_o, "d_o", q.shape)):
-        _need(t, n, shp, q.dtype)
-    _need(lse, "lse", (B, Hq, L), torch.float32)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+        _need(t, n, shp, q.dtype, q.device)
+    _need(lse, "lse", (B, Hq, L), torch.float32, q.device)
+    dq = torch.empty_like(q) if dq is None else _out(dq, "dq", q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _out(dk, "dk", k.shape, k.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _out(dv, "dv", v.shape, v.dtype, q.device)
     ws, nb = _workspace(bd_attn_bwd_workspace_size(B, L, Hq, Hkv, d), q.device, workspace)
     st = lib.bd_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
                          _ptr(ws), nb, B, L, Hq, Hkv, d, block_size, float(softmax_scale), _dtype_code(q),
@@ -117,18 +141,21 @@ def bd_attn_decode_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_start, pr
     """One block per sequence against its prefix cache -> (o, lse)."""
     n, T, Hq, d = q_blk.shape
     Hkv = k_blk.shape[2]
+    dev = q_blk.device
     _need(q_blk, "q_blk")
-    _need(k_blk, "k_blk", (n, T, Hkv, d), q_blk.dtype)
-    _need(v_blk, "v_blk", (n, T, Hkv, d), q_blk.dtype)
+    _need(k_blk, "k_blk", (n, T, Hkv, d), q_blk.dtype, dev)
+    _need(v_blk, "v_blk", (n, T, Hkv, d), q_blk.dtype, dev)
     for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
         if t is not None:
-            _need(t, name, None, q_blk.dtype)
-    _need(prefix_start, "prefix_start", (n,), torch.int64)
-    _need(prefix_len, "prefix_len", (n,), torch.int32)
-    if o is None:
-        o = torch.empty_like(q_blk)
+            _need(t, name, None, q_blk.dtype, dev)
+            if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, d):
+                raise ValueError(f"{name} must be [rows, {Hkv}, {d}]")
+    _need(prefix_start, "prefix_start", (n,), torch.int64, dev)
+    _need(prefix_len, "prefix_len", (n,), torch.int32, dev)
+    o = torch.empty_like(q_blk) if o is None else _out(o, "o", q_blk.shape, q_blk.dtype, dev)
+    lse = _out(lse, "lse", (n, Hq, T), torch.float32, dev)
     if lse is None and want_lse:
-        lse = torch.empty((n, Hq, T), dtype=torch.float32, device=q_blk.device)
+        lse = torch.empty((n, Hq, T), dtype=torch.float32, device=dev)
     ws, nb = _workspace(bd_attn_decode_workspace_size(n, T, max_prefix_len, Hq, Hkv, d), q_blk.device, workspace)
     st = lib.bd_attn_decode_block(_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(prefix_start), _ptr(prefix_len), int(max_prefix_len), _ptr(o), _ptr(lse),
@@ -159,17 +186,14 @@ def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold, fallba
     V = logits.shape[1] if vocab is None else int(vocab)
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
-    _need(tokens, "tokens", (rows,), torch.int32)
-    _need(masked, "masked", (rows,), torch.uint8)
     dev = logits.device
-    if want_rows:
-        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
-        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
-    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
-    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    _need(tokens, "tokens", (rows,), torch.int32, dev)
+    _need(masked, "masked", (rows,), torch.uint8, dev)
+    conf, pred, n_committed, n_masked_left = _row_outputs(rows, n_seq, dev, want_rows, conf, pred, n_committed,
+                                                          n_masked_left)
     ws, nb = _workspace(bd_confidence_commit_workspace_size(n_seq, blk_len, V), dev, workspace)
     if isinstance(threshold, torch.Tensor):
-        _need(threshold, "threshold", (rows,), torch.float32)
+        _need(threshold, "threshold", (rows,), torch.float32, dev)
         st = lib.bd_confidence_commit_rowwise(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
                                               _ptr(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf),
                                               _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _ptr(ws), nb,
@@ -197,8 +221,13 @@ def bd_confidence_commit_noalloc(logits, tokens, masked, blk_len: int, threshold
     V = logits.shape[1] if vocab is None else int(vocab)
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
-    _need(tokens, "tokens", (rows,), torch.int32)
-    _need(masked, "masked", (rows,), torch.uint8)
+    dev = logits.device
+    _need(tokens, "tokens", (rows,), torch.int32, dev)
+    _need(masked, "masked", (rows,), torch.uint8, dev)
+    conf = _out(conf, "conf", (rows,), torch.float32, dev)
+    pred = _out(pred, "pred", (rows,), torch.int32, dev)
+    n_committed = _out(n_committed, "n_committed", (n_seq,), torch.int32, dev)
+    n_masked_left = _out(n_masked_left, "n_masked_left", (n_seq,), torch.int32, dev)
     st = lib.bd_confidence_commit_noalloc(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
                                           float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf),
                                           _ptr(pred), _ptr(n_committed), _ptr(n_masked_left), _stream(stream))
@@ -228,14 +257,13 @@ def bd_lmhead_commit(hidden, weight, tokens, masked, blk_len: int, threshold: fl
             raise ValueError(f"{name} must be a bf16 device tensor with unit stride along the hidden dimension")
     if weight.shape[1] != H:
         raise ValueError("weight must be [vocab, hidden]")
-    _need(tokens, "tokens", (rows,), torch.int32)
-    _need(masked, "masked", (rows,), torch.uint8)
     dev = hidden.device
-    if want_rows:
-        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
-        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
-    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
-    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    if weight.device != dev:
+        raise ValueError(f"weight is on {weight.device}, expected {dev}")
+    _need(tokens, "tokens", (rows,), torch.int32, dev)
+    _need(masked, "masked", (rows,), torch.uint8, dev)
+    conf, pred, n_committed, n_masked_left = _row_outputs(rows, n_seq, dev, want_rows, conf, pred, n_committed,
+                                                          n_masked_left)
     ws, nb = _workspace(bd_lmhead_commit_workspace_size(n_seq, blk_len, V), dev, workspace)
     st = lib.bd_lmhead_commit(_ptr(hidden), hidden.stride(0), _ptr(weight), weight.stride(0), n_seq, blk_len, H, V,
                               float(threshold), int(fallback), _ptr(tokens), _ptr(masked), _ptr(conf), _ptr(pred),
@@ -263,14 +291,11 @@ def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold
     V = logits.shape[1] if vocab is None else int(vocab)
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
-    _need(tokens, "tokens", (rows,), torch.int32)
-    _need(masked, "masked", (rows,), torch.uint8)
     dev = logits.device
-    if want_rows:
-        conf = torch.empty(rows, dtype=torch.float32, device=dev) if conf is None else conf
-        pred = torch.empty(rows, dtype=torch.int32, device=dev) if pred is None else pred
-    n_committed = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_committed is None else n_committed
-    n_masked_left = torch.empty(n_seq, dtype=torch.int32, device=dev) if n_masked_left is None else n_masked_left
+    _need(tokens, "tokens", (rows,), torch.int32, dev)
+    _need(masked, "masked", (rows,), torch.uint8, dev)
+    conf, pred, n_committed, n_masked_left = _row_outputs(rows, n_seq, dev, want_rows, conf, pred, n_committed,
+                                                          n_masked_left)
     ws, nb = _workspace(bd_confidence_commit_sampled_workspace_size(n_seq, blk_len, V), dev, workspace)
     st = lib.bd_confidence_commit_sampled(_ptr(logits), logits.stride(0), n_seq, blk_len, V, _dtype_code(logits),
                                           float(temperature), int(seed), int(step), int(top_k), float(top_p),
@@ -289,15 +314,21 @@ def bd_attn_decode_block_paged(q_blk, k_blk, v_blk, k_pages, v_pages, block_tabl
     prefix_len int32 [n_seq].  Returns (o, lse)."""
     n_seq, T, Hq, d = q_blk.shape
     Hkv = k_blk.shape[2]
-    for t, name in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_pages, "k_pages"), (v_pages, "v_pages")):
-        _need(t, name, dtype=torch.bfloat16)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(prefix_len, "prefix_len", (n_seq,), torch.int32)
+    dev = q_blk.device
+    _need(q_blk, "q_blk", dtype=torch.bfloat16)
+    _need(k_blk, "k_blk", (n_seq, T, Hkv, d), torch.bfloat16, dev)
+    _need(v_blk, "v_blk", (n_seq, T, Hkv, d), torch.bfloat16, dev)
+    for t, name in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, dtype=torch.bfloat16, device=dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, d):
+            raise ValueError(f"{name} must be [n_pages * page_size, {Hkv}, {d}]")
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    _need(prefix_len, "prefix_len", (n_seq,), torch.int32, dev)
     if block_table.dim() != 2 or block_table.shape[0] != n_seq:
         raise ValueError("block_table must be [n_seq, max_pages]")
-    dev = q_blk.device
-    o = torch.empty_like(q_blk) if o is None else o
-    lse = torch.empty((n_seq, Hq, T), dtype=torch.float32, device=dev) if lse is None else lse
+    o = torch.empty_like(q_blk) if o is None else _out(o, "o", q_blk.shape, torch.bfloat16, dev)
+    lse = torch.empty((n_seq, Hq, T), dtype=torch.float32, device=dev) if lse is None else \
+        _out(lse, "lse", (n_seq, Hq, T), torch.float32, dev)
     ws, nb = _workspace(bd_attn_decode_workspace_size(n_seq, T, max_prefix_len, Hq, Hkv, d), dev, workspace)
     st = lib.bd_attn_decode_block_paged(_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pages), _ptr(v_pages),
                                         _ptr(block_table), block_table.shape[1], page_size, _ptr(prefix_len),
@@ -311,12 +342,19 @@ def bd_kv_append_block(k_blk, v_blk, k_pages, v_pages, block_table, page_size: i
                        stream=None):
     """Append finished blocks (n_masked_left == 0, or all) to the paged cache; prefix_len grows in place."""
     n_seq, T, Hkv, d = k_blk.shape
-    for t, name in ((k_blk, "k_blk"), (v_blk, "v_blk"), (k_pages, "k_pages"), (v_pages, "v_pages")):
-        _need(t, name, dtype=torch.bfloat16)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(prefix_len, "prefix_len", (n_seq,), torch.int32)
+    dev = k_blk.device
+    _need(k_blk, "k_blk", dtype=torch.bfloat16)
+    _need(v_blk, "v_blk", (n_seq, T, Hkv, d), torch.bfloat16, dev)
+    for t, name in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, name, dtype=torch.bfloat16, device=dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, d):
+            raise ValueError(f"{name} must be [n_pages * page_size, {Hkv}, {d}]")
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    if block_table.dim() != 2 or block_table.shape[0] != n_seq:
+        raise ValueError("block_table must be [n_seq, max_pages]")
+    _need(prefix_len, "prefix_len", (n_seq,), torch.int32, dev)
     if n_masked_left is not None:
-        _need(n_masked_left, "n_masked_left", (n_seq,), torch.int32)
+        _need(n_masked_left, "n_masked_left", (n_seq,), torch.int32, dev)
     st = lib.bd_kv_append_block(_ptr(k_blk), _ptr(v_blk), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                 block_table.shape[1], page_size, _ptr(prefix_len),
                                 _ptr(n_masked_left) if n_masked_left is not None else None, n_seq, T, Hkv, d, BD_BF16,
