@@ -184,6 +184,8 @@ def bd_confidence_commit(logits, tokens, masked, blk_len: int, threshold, fallba
         raise ValueError("logits rows must be a multiple of blk_len")
     n_seq = rows // blk_len
     V = logits.shape[1] if vocab is None else int(vocab)
+    if V > logits.shape[1]:
+        raise ValueError(f"vocab {V} exceeds the {logits.shape[1]} logits per row")
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
     dev = logits.device
@@ -219,6 +221,8 @@ def bd_confidence_commit_noalloc(logits, tokens, masked, blk_len: int, threshold
         raise ValueError("logits rows must be a multiple of blk_len")
     n_seq = rows // blk_len
     V = logits.shape[1] if vocab is None else int(vocab)
+    if V > logits.shape[1]:
+        raise ValueError(f"vocab {V} exceeds the {logits.shape[1]} logits per row")
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
     dev = logits.device
@@ -289,6 +293,8 @@ def bd_confidence_commit_sampled(logits, tokens, masked, blk_len: int, threshold
         raise ValueError("logits rows must be a multiple of blk_len")
     n_seq = rows // blk_len
     V = logits.shape[1] if vocab is None else int(vocab)
+    if V > logits.shape[1]:
+        raise ValueError(f"vocab {V} exceeds the {logits.shape[1]} logits per row")
     if not logits.is_cuda or logits.stride(1) != 1:
         raise ValueError("logits must be a device tensor with unit stride along the vocabulary")
     dev = logits.device

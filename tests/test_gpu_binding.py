@@ -78,6 +78,8 @@ def test_commit_outputs_checked():
             bd.bd_confidence_commit_noalloc(logits, tokens, masked, 32, 0.9, **kw)
         with pytest.raises(ValueError):
             bd.bd_confidence_commit_sampled(logits, tokens, masked, 32, 0.9, **kw)
+    with pytest.raises(ValueError):   # a vocabulary wider than the rows would read past the last row
+        bd.bd_confidence_commit(logits, tokens, masked, 32, 0.9, vocab=V + 8)
     w, h = _bf16(V, 64), _bf16(rows, 64)
     with pytest.raises(ValueError):
         bd.bd_lmhead_commit(h, w, tokens, masked, 32, 0.9, conf=torch.empty(rows, dtype=torch.float64,
