@@ -99,11 +99,13 @@ def test_threshold_extremes_and_partial_masks():
     run_case(c["logits"], "bf16", c["tokens"], none, 32, 0.5)
 
 
-def test_long_blocks():
-    banner("commit blk_len=1000")
-    c = W.commit_inputs(2, 1000, 700, "f32", seed=12, masked_frac=0.9, logit_std=3.0)
+@pytest.mark.parametrize("blk_len,dtype", [(1000, "f32"), (1024, "bf16"), (1024, "f32")])
+def test_long_blocks(blk_len, dtype):
+    """Blocks up to the longest the commit takes (1024 rows)."""
+    banner(f"commit blk_len={blk_len} {dtype}")
+    c = W.commit_inputs(2, blk_len, 700, dtype, seed=12, masked_frac=0.9, logit_std=3.0)
     for T in (0.9, 0.999):
-        run_case(c["logits"], "f32", c["tokens"], c["masked"], 1000, T)
+        run_case(c["logits"], dtype, c["tokens"], c["masked"], blk_len, T)
 
 
 def test_batched_loop_scale():

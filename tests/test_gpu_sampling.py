@@ -67,6 +67,14 @@ def test_decode_step_workload():
             run_case(c["logits"], "bf16", c["tokens"], c["masked"], 32, T, 1.0, seed, step)
 
 
+def test_longest_blocks():
+    """Blocks of the longest length the commit takes (1024 rows)."""
+    banner("sampled commit blk_len=1024")
+    c = W.commit_inputs(2, 1024, 700, "bf16", seed=31, masked_frac=0.9, logit_std=3.0)
+    for T in (0.5, 0.999):
+        run_case(c["logits"], "bf16", c["tokens"], c["masked"], 1024, T, 1.0, seed=9, step=3)
+
+
 @pytest.mark.parametrize("V,stride", [(5003, None), (5003, 5008), (4096, 4100), (77, None)])
 def test_ragged_vocab_and_strides(V, stride):
     banner(f"sampled commit V={V} stride={stride}")
