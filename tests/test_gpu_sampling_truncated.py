@@ -188,6 +188,14 @@ def test_fp32_full_vocabulary():
     run_case(c["logits"], "f32", c["tokens"], c["masked"], 32, 0.5, 1.3, seed=8, step=5, top_k=0, top_p=0.95)
 
 
+def test_bf16_full_vocabulary():
+    """bf16 logits at the largest vocabulary the register-held row allows (155648 ids)."""
+    banner("truncated sampling bf16 V=155648")
+    c = W.commit_inputs(1, 32, 155648, "bf16", seed=33, masked_frac=0.25, logit_std=1.5)
+    run_case(c["logits"], "bf16", c["tokens"], c["masked"], 32, 0.5, 1.0, seed=8, step=6, top_k=200, top_p=0.9)
+    run_case(c["logits"], "bf16", c["tokens"], c["masked"], 32, 0.5, 0.8, seed=8, step=7, top_k=0, top_p=0.95)
+
+
 def test_batched_loop_scale():
     """The 64-sequence decode step (2048 rows of 151936 bf16 logits, 60 % masked) with top-p 0.9;
     a sample of rows is checked against the oracle."""
