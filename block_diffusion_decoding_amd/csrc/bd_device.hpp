@@ -133,12 +133,15 @@ __device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l of
 // the wave writes bytes [lds_base + 16 l, +16).  Issued through inline asm so
 // that the compiler does not fence every later LDS read on it; the caller
-// waits with vm_wait<N>() before a barrier.  M0 is restored afterwards.
+// waits with vm_wait<N>() before a barrier.  M0 is restored afterwards.  A
+// scalar write of M0 needs one wait state before an LDS-DMA load reads it (the
+// compiler keeps that distance in the code it emits itself), hence the s_nop.
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -153,6 +156,7 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -198,11 +202,34 @@ __device__ __forceinline__ void tile_dma_offsets(uint32_t* off, int64_t rs, int 
     off[i] = (uint32_t)((r * rs + 8 * c) * 2);
   }
 }
+// With four waves each wave issues four 1 KB copies to consecutive LDS
+// addresses; they go in one asm statement, so M0 is saved and restored once and
+// each M0 write is followed by the one wait state the copy that reads it needs.
 template <int NW>
 __device__ __forceinline__ void tile_dma_full(uint32_t lds_tile, const uint16_t* g_tile, const uint32_t* off,
                                               int wave) {
-#pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) lds_dma16_s(g_tile, off[i], lds_tile + (wave * (16 / NW) + i) * 1024);
+  static_assert(NW == 4, "four copies per wave");
+  const uint32_t l0 = lds_tile + wave * 4 * 1024;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(g_tile), "s"(l0), "s"(l0 + 1024),
+        "s"(l0 + 2048), "s"(l0 + 3072)
+      : "memory");
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
