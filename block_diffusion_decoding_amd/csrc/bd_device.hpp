@@ -176,17 +176,41 @@ __device__ __forceinline__ void vm_wait() {
 // last valid row) into the swizzled LDS tile at byte address `lds_tile`.
 // The tile is 16 wave-instructions of 1 KB (4 rows each); wave w of NW issues
 // instructions w*16/NW .. +16/NW-1.
+// Two copies to consecutive 1 KB LDS blocks in one asm statement (M0 saved and
+// restored once, one wait state after each M0 write).
+__device__ __forceinline__ void lds_dma16_x2(const void* g0, const void* g1, uint32_t l0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g0), "v"(g1), "s"(l0), "s"(l0 + 1024)
+      : "memory");
+}
+
 template <int NW>
 __device__ __forceinline__ void tile_dma(uint32_t lds_tile, const uint16_t* g, int64_t rs, int row0, int nrows,
                                          int wave, int lane) {
+  static_assert(NW == 4 || NW == 8, "two or four copies per wave");
+  constexpr int kPer = 16 / NW;
+  const uint16_t* src[kPer];
 #pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) {
-    const int n = wave * (16 / NW) + i;
+  for (int i = 0; i < kPer; ++i) {
+    const int n = wave * kPer + i;
     const int r = 4 * n + (lane >> 4);
     const int c = (lane & 15) ^ tile_swz(r);
     const int row = min(row0 + r, nrows - 1);
-    lds_dma16(g + row * rs + 8 * c, lds_tile + n * 1024);
+    src[i] = g + row * rs + 8 * c;
   }
+  const uint32_t l0 = lds_tile + wave * kPer * 1024;
+#pragma unroll
+  for (int i = 0; i < kPer; i += 2) lds_dma16_x2(src[i], src[i + 1], l0 + i * 1024);
 }
 
 // The same copy for a tile whose 64 rows all exist: the per-lane byte offsets
