@@ -470,8 +470,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, const int wid) {
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   auto issue = [&](int t) {
     const uint32_t st = lds0 + (uint32_t)(t & 1) * kDqStage;
-    tile_dma<kDqNW>(st, kb, kv_rs, t * 64, kend_wg, wave, lane);
-    tile_dma<kDqNW>(st + kTileBytes, vb, kv_rs, t * 64, kend_wg, wave, lane);
+    static_assert(kDqNW == 8, "eight waves share the K and V copies");
+    tile_dma_pair8(st, kb, st + kTileBytes, vb, kv_rs, t * 64, kend_wg, wave, lane);
   };
   if (ntiles > 0) issue(0);
 

@@ -194,23 +194,66 @@ __device__ __forceinline__ void lds_dma16_x2(const void* g0, const void* g1, uin
       : "memory");
 }
 
+// Four copies in one asm statement, to any four 1 KB LDS blocks.
+__device__ __forceinline__ void lds_dma16_x4(const void* g0, const void* g1, const void* g2, const void* g3,
+                                             uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g0), "v"(g1), "v"(g2), "v"(g3), "s"(l0), "s"(l1), "s"(l2), "s"(l3)
+      : "memory");
+}
+
+// Source address of copy i of this wave's share of a clamped tile (see tile_dma).
+template <int NW>
+__device__ __forceinline__ const uint16_t* tile_src(const uint16_t* g, int64_t rs, int row0, int nrows, int wave,
+                                                    int lane, int i) {
+  const int n = wave * (16 / NW) + i;
+  const int r = 4 * n + (lane >> 4);
+  const int c = (lane & 15) ^ tile_swz(r);
+  const int row = min(row0 + r, nrows - 1);
+  return g + row * rs + 8 * c;
+}
+
 template <int NW>
 __device__ __forceinline__ void tile_dma(uint32_t lds_tile, const uint16_t* g, int64_t rs, int row0, int nrows,
                                          int wave, int lane) {
   static_assert(NW == 4 || NW == 8, "two or four copies per wave");
   constexpr int kPer = 16 / NW;
-  const uint16_t* src[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int n = wave * kPer + i;
-    const int r = 4 * n + (lane >> 4);
-    const int c = (lane & 15) ^ tile_swz(r);
-    const int row = min(row0 + r, nrows - 1);
-    src[i] = g + row * rs + 8 * c;
-  }
   const uint32_t l0 = lds_tile + wave * kPer * 1024;
-#pragma unroll
-  for (int i = 0; i < kPer; i += 2) lds_dma16_x2(src[i], src[i + 1], l0 + i * 1024);
+  if constexpr (kPer == 2) {
+    lds_dma16_x2(tile_src<NW>(g, rs, row0, nrows, wave, lane, 0), tile_src<NW>(g, rs, row0, nrows, wave, lane, 1),
+                 l0);
+  } else {
+    lds_dma16_x4(tile_src<NW>(g, rs, row0, nrows, wave, lane, 0), tile_src<NW>(g, rs, row0, nrows, wave, lane, 1),
+                 tile_src<NW>(g, rs, row0, nrows, wave, lane, 2), tile_src<NW>(g, rs, row0, nrows, wave, lane, 3),
+                 l0, l0 + 1024, l0 + 2048, l0 + 3072);
+  }
+}
+
+// Two tiles with the same rows (K and V of one key range) copied by eight
+// waves, each wave's four copies in one asm statement.
+__device__ __forceinline__ void tile_dma_pair8(uint32_t lds_a, const uint16_t* ga, uint32_t lds_b,
+                                               const uint16_t* gb, int64_t rs, int row0, int nrows, int wave,
+                                               int lane) {
+  const uint32_t la = lds_a + wave * 2 * 1024, lb = lds_b + wave * 2 * 1024;
+  lds_dma16_x4(tile_src<8>(ga, rs, row0, nrows, wave, lane, 0), tile_src<8>(ga, rs, row0, nrows, wave, lane, 1),
+               tile_src<8>(gb, rs, row0, nrows, wave, lane, 0), tile_src<8>(gb, rs, row0, nrows, wave, lane, 1),
+               la, la + 1024, lb, lb + 1024);
 }
 
 // The same copy for a tile whose 64 rows all exist: the per-lane byte offsets
