@@ -468,10 +468,17 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, const int wid) {
   const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
   const uint16_t* kb = p.k + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
   const uint16_t* vb = p.v + (int64_t)b * L * kv_rs + (int64_t)kvh * D;
+  uint32_t kv_off[2];
+  tile_dma_offsets<kDqNW>(kv_off, kv_rs, wave, lane);
   auto issue = [&](int t) {
     const uint32_t st = lds0 + (uint32_t)(t & 1) * kDqStage;
     static_assert(kDqNW == 8, "eight waves share the K and V copies");
-    tile_dma_pair8(st, kb, st + kTileBytes, vb, kv_rs, t * 64, kend_wg, wave, lane);
+    if (t + 1 < ntiles) {   // all 64 rows exist: fixed per-lane offsets from the tile's base
+      const int64_t row0 = (int64_t)t * 64 * kv_rs;
+      tile_dma_pair8_full(st, kb + row0, st + kTileBytes, vb + row0, kv_off, wave);
+    } else {
+      tile_dma_pair8(st, kb, st + kTileBytes, vb, kv_rs, t * 64, kend_wg, wave, lane);
+    }
   };
   if (ntiles > 0) issue(0);
 

@@ -256,6 +256,33 @@ __device__ __forceinline__ void tile_dma_pair8(uint32_t lds_a, const uint16_t* g
                la, la + 1024, lb, lb + 1024);
 }
 
+// K and V rows of one whole 64-row tile (both with the same row stride) copied
+// by eight waves: per-lane byte offsets from tile_dma_offsets<8>, wave-uniform
+// tile bases; each wave's four copies in one asm statement.
+__device__ __forceinline__ void tile_dma_pair8_full(uint32_t lds_a, const uint16_t* ga_tile, uint32_t lds_b,
+                                                    const uint16_t* gb_tile, const uint32_t* off, int wave) {
+  const uint32_t la = lds_a + wave * 2 * 1024, lb = lds_b + wave * 2 * 1024;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %4\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "s"(ga_tile), "s"(gb_tile), "s"(la), "s"(la + 1024), "s"(lb), "s"(lb + 1024)
+      : "memory");
+}
+
 // The same copy for a tile whose 64 rows all exist: the per-lane byte offsets
 // (from tile_dma_offsets) do not depend on the tile, only the uniform base
 // `g_tile` (= row row0 of the matrix) does.
