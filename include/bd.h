@@ -34,9 +34,11 @@
  *     gives the hipError_t).  Faults inside a kernel surface at the caller's
  *     next synchronisation.
  *   - The library keeps no mutable global state except a thread-local last HIP
- *     error (and, for bd_confidence_commit_noalloc only, a fixed device scratch
- *     array per GPU); calls on different streams may run concurrently as long as
- *     their output and workspace buffers do not overlap.
+ *     error, values set once per process and never changed afterwards (kernel
+ *     launch attributes, each device's compute-unit count; set under a lock or
+ *     a once-flag) and, for bd_confidence_commit_noalloc only, a fixed device
+ *     scratch array per GPU; calls on different streams may run concurrently as
+ *     long as their output and workspace buffers do not overlap.
  */
 #ifndef BD_H_
 #define BD_H_
