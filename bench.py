@@ -518,6 +518,40 @@ def main():
     f3_ms = np.array([a.elapsed_time(b_) for a, b_ in f3_ev])
     del q3, k3, v3, o3, lse3
 
+    # --------------- the tiny fp32 workload: one forward and one commit step, GPU time per launch
+    w1 = W.WORKLOADS["tiny_f32"]
+    inp1 = W.attention_inputs(w1.batch, w1.seqlen, w1.n_q_heads, w1.n_kv_heads, w1.head_dim, "f32", w1.seed)
+    q1t, k1t, v1t = (torch.from_numpy(np.ascontiguousarray(inp1[n], dtype=np.float32)).to(dev) for n in ("q", "k", "v"))
+    o1t = torch.empty_like(q1t)
+    lse1t = torch.empty((w1.batch, w1.n_q_heads, w1.seqlen), dtype=torch.float32, device=dev)
+    ct1 = W.commit_inputs(1, w1.block_size, w1.vocab, "f32", w1.seed, masked_frac=w1.masked_frac,
+                          logit_std=w1.logit_std)
+    lg1t = torch.from_numpy(np.ascontiguousarray(ct1["logits"], dtype=np.float32)).to(dev)
+    n_tiny = 40      # one token state per commit launch, so every launch sees the same masked rows
+    tok1t = [torch.from_numpy(ct1["tokens"].copy()).to(dev) for _ in range(n_tiny)]
+    msk1t = [torch.from_numpy(ct1["masked"].copy()).to(dev) for _ in range(n_tiny)]
+    cws1t = torch.empty(bd.bd_confidence_commit_workspace_size(1, w1.block_size, w1.vocab), dtype=torch.uint8,
+                        device=dev)
+    tok0t, msk0t = tok1t[0].clone(), msk1t[0].clone()
+    conf1t = torch.empty(w1.block_size, dtype=torch.float32, device=dev)
+    pred1t = torch.empty(w1.block_size, dtype=torch.int32, device=dev)
+    ncom1t = torch.empty(1, dtype=torch.int32, device=dev)
+    nleft1t = torch.empty(1, dtype=torch.int32, device=dev)
+    tiny_fwd_us, tiny_com_us = [], []
+    for rnd in range(3):   # the first round warms up and is not kept
+        t_us = primed([lambda: bd.bd_attn_fwd(q1t, k1t, v1t, w1.block_size, o=o1t, lse=lse1t)] * n_tiny)
+        for t_, m_ in zip(tok1t, msk1t):
+            t_.copy_(tok0t)
+            m_.copy_(msk0t)
+        c_us = primed([lambda i=i: bd.bd_confidence_commit(lg1t, tok1t[i], msk1t[i], w1.block_size, w1.threshold,
+                                                           conf=conf1t, pred=pred1t, n_committed=ncom1t,
+                                                           n_masked_left=nleft1t, workspace=cws1t)
+                       for i in range(n_tiny)])
+        if rnd:
+            tiny_fwd_us.extend(t_us)
+            tiny_com_us.extend(c_us)
+    del q1t, k1t, v1t, o1t, lse1t, lg1t, tok1t, msk1t
+
     # --------------------------------------------------------- CPU oracle sample
     cpu = None
     if not args.no_cpu:
@@ -609,6 +643,8 @@ def main():
                              "us_p10": round(float(np.percentile(com1_us, 10)), 2),
                              "us_p90": round(float(np.percentile(com1_us, 90)), 2),
                              "GBps": round(com1_bytes / (np.median(com1_us) * 1e-6) / 1e9, 1)},
+        "tiny_f32_latency": {"fwd_us_median": round(float(np.median(tiny_fwd_us)), 2),
+                             "commit_us_median": round(float(np.median(tiny_com_us)), 2)},
     }
     print(json.dumps(line), flush=True)
 
@@ -791,6 +827,20 @@ def cpu_baseline(wl, budget_s: float, cfg2: dict, loop_sample: dict):
     OC.confidence_commit(lg, np.full(R, -1, np.int32), np.ones(R, np.uint8), R, cfg2["threshold"])
     t_com = time.perf_counter() - t0
     legs["decode_step_4096"] = {"GBps": round(dec_bytes / t_dec / 1e9, 4), "s": round(t_dec, 3)}
+
+    # the tiny fp32 workload in full: block attention over 128 tokens and one commit step
+    w1 = W.WORKLOADS["tiny_f32"]
+    i1 = W.attention_inputs(w1.batch, w1.seqlen, w1.n_q_heads, w1.n_kv_heads, w1.head_dim, "f32", w1.seed)
+    c1 = W.commit_inputs(1, w1.block_size, w1.vocab, "f32", w1.seed, masked_frac=w1.masked_frac,
+                         logit_std=w1.logit_std)
+    t0 = time.perf_counter()
+    OA.attn_fwd(*(np.asarray(i1[n], np.float64) for n in ("q", "k", "v")), w1.block_size)
+    t_tf = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    OC.confidence_commit(np.asarray(c1["logits"], np.float64), c1["tokens"], c1["masked"], w1.block_size,
+                         w1.threshold)
+    t_tc = time.perf_counter() - t0
+    legs["tiny_f32"] = {"fwd_us": round(t_tf * 1e6, 1), "commit_us": round(t_tc * 1e6, 1)}
     legs["commit_32x151936"] = {"GBps": round(lg.size * 2 / t_com / 1e9, 4), "s": round(t_com, 3)}
 
     # backward on the last 1024 tokens of one group (2 query heads sharing one KV head)

@@ -44,7 +44,53 @@ __device__ void attend_row(const RowVec& q, int nkeys, int d, float scale_log2, 
                            float* lse_out, int lane) {
   float m = kNegInf, l = 0.f;
   float acc[kMaxPerLane] = {0.f, 0.f};
-  for (int j = 0; j < nkeys; ++j) {
+  // Eight keys per step: their loads are in flight together and the online
+  // update takes their common maximum (the same algebra as one key at a time).
+  constexpr int kU = 8;
+  int j = 0;
+  for (; j + kU <= nkeys; j += kU) {
+    float kx[kU][kMaxPerLane], vx[kU][kMaxPerLane];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float* kr;
+      const float* vr;
+      kv(j + u, kr, vr);
+#pragma unroll
+      for (int e = 0; e < kMaxPerLane; ++e) {
+        const int c = lane + 64 * e;
+        kx[u][e] = c < d ? kr[c] : 0.f;
+        vx[u][e] = c < d ? vr[c] : 0.f;
+      }
+    }
+    float s[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < kMaxPerLane; ++e) part += q.x[e] * kx[u][e];
+      s[u] = wave_sum(part) * scale_log2;
+    }
+    float m_new = m;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) m_new = fmaxf(m_new, s[u]);
+    const float alpha = exp2f(m - m_new);
+    float pu[kU], psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      pu[u] = exp2f(s[u] - m_new);
+      psum += pu[u];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      float pv = 0.f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) pv += pu[u] * vx[u][e];
+      acc[e] = acc[e] * alpha + pv;
+    }
+    m = m_new;
+  }
+  for (; j < nkeys; ++j) {
     const float* kr;
     const float* vr;
     kv(j, kr, vr);
