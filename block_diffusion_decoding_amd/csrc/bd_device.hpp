@@ -70,15 +70,7 @@ __device__ __forceinline__ int key_limit(int i, int seqlen, int block_size) {
 // supply as the B operand of the following 32x32x16 product over those keys.
 __device__ __forceinline__ int sigma32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <typename T>
-__device__ __forceinline__ T wave_shfl_xor(T v, int m) { return __shfl_xor(v, m, 64); }
-
 // LDS-free reductions across the 64 lanes of a wave.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -149,21 +141,6 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
       : "memory");
 }
 
-// The same copy addressed as a wave-uniform 64-bit base (held in scalar
-// registers) plus a 32-bit per-lane byte offset.
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_base)
-      : "memory");
-}
-
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -171,11 +148,6 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Copy this wave's share of a 64-row tile (rows row0 .. row0+63 of a row-major
-// bf16 matrix with row stride `rs` elements; rows >= nrows are clamped to the
-// last valid row) into the swizzled LDS tile at byte address `lds_tile`.
-// The tile is 16 wave-instructions of 1 KB (4 rows each); wave w of NW issues
-// instructions w*16/NW .. +16/NW-1.
 // Two copies to consecutive 1 KB LDS blocks in one asm statement (M0 saved and
 // restored once, one wait state after each M0 write).
 __device__ __forceinline__ void lds_dma16_x2(const void* g0, const void* g1, uint32_t l0) {
@@ -229,6 +201,11 @@ __device__ __forceinline__ const uint16_t* tile_src(const uint16_t* g, int64_t r
   return g + row * rs + 8 * c;
 }
 
+// Copy this wave's share of a 64-row tile (rows row0 .. row0+63 of a row-major
+// bf16 matrix with row stride `rs` elements; rows >= nrows are clamped to the
+// last valid row) into the swizzled LDS tile at byte address `lds_tile`.
+// The tile is 16 wave-instructions of 1 KB (4 rows each); wave w of NW issues
+// instructions w*16/NW .. +16/NW-1.
 template <int NW>
 __device__ __forceinline__ void tile_dma(uint32_t lds_tile, const uint16_t* g, int64_t rs, int row0, int nrows,
                                          int wave, int lane) {
@@ -354,15 +331,6 @@ __device__ __forceinline__ bf16x8 cat_i16x4(i16x4 lo, i16x4 hi) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, w);
-}
-
-// A operand (rows = head dim, k = 16 tile rows 16*s .. 16*s+15) of a 32x32x16
-// product, read transposed from a row-major swizzled tile T[row][d]: lane l
-// gets T[16s + 8(l/32) + r][32 db + l % 32] for r = 0..7.
-__device__ __forceinline__ bf16x8 tile_read_t(uint32_t lds_tile, int db, int s, int lane) {
-  const int row0 = 16 * s + 8 * (lane >> 5);
-  const int dbase = 32 * db + 16 * ((lane >> 4) & 1);
-  return cat_i16x4(tile_read_t4(lds_tile, row0, dbase, lane), tile_read_t4(lds_tile, row0 + 4, dbase, lane));
 }
 
 // A operand (rows = head dim, k = 32 tile rows 32*s .. 32*s+31) of a 16x16x32
