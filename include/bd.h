@@ -111,10 +111,11 @@ bd_status bd_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   dq  [batch, seqlen, n_q_heads, head_dim]       out
  *   dk, dv [batch, seqlen, n_kv_heads, head_dim]   out (summed over the query
  *        heads of each group)
- *   workspace of bd_attn_bwd_workspace_size() bytes (holds, per row, D =
- *        rowsum(d_o * o) and lse * log2(e) in float32, and the counters that
- *        hand out work items to the compute units); contents on entry are
- *        ignored.
+ *   workspace of bd_attn_bwd_workspace_size() bytes (bf16: two float32
+ *        arrays [batch, n_q_heads, seqlen rounded up to 64] holding -D, with
+ *        D = rowsum(d_o * o), and -lse / scale, then the counters that hand
+ *        out work items to the compute units; fp32: D per row); contents on
+ *        entry are ignored.
  *
  * Supported: as bd_attn_fwd.  Deterministic: every output element is summed
  * by one workgroup in one fixed order (the counters only decide which
